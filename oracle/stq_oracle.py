@@ -1,0 +1,381 @@
+"""STQ1_0 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously-correct NumPy implementation of what the STQ1_0
+sparse-ternary quantized matmul computes.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  It shares no code with the HIP library (no kernels, headers,
+tables or helpers); the only thing both sides see is the seeded inputs from
+``synth_inputs``.
+
+Sources ("the pages"), cited by title/address and section:
+  [LEMMY]  lemmy.durstig.online post 66506 (a relayed Reddit post), with run-in
+           paragraphs "Four weights, five bits", "Scale and zero position are
+           fit together", "Full-Hessian scoring", "Runtime".
+  [AGI]    "Tencent compresses 770B Hunyuan Hy4 Preview into 214 GiB at ~2.38
+           bits per weight" (agihunt.info), sections "Four weights, five bits",
+           "Fitting and runtime".
+  [TRAIC]  "Tencent's 200GB Hy4-preview: a 7x compression claim that needs a
+           second look" (traictory.com), section "MIX-STQ1_0: where the bits go".
+  [ALPHA]  "AngelSlim Shrinks Tencent's 1.5TB Hy4-Preview to 214 GiB at 6x
+           Compression" (alphasignal.ai), summary bullets and section
+           "How STQ1_0 works".
+
+What the pages fix: each group of four weights takes values in {-d, 0, +d}
+with exactly one zero lane; 4 zero positions x 8 sign choices = 32 patterns,
+5 bits per group ([LEMMY] "Four weights, five bits"); the 5 bits are a 4-bit
+code plus a 1-bit table select into a 32-entry codebook, and one fp16 scale is
+shared by 256 weights, 42 bytes per block ([ALPHA] "How STQ1_0 works").  The
+encoder alternates a weighted-least-squares fit of d with an
+imatrix-weighted choice of the zero lane, for three rounds, and is compared
+against an amax-scaled original encoder ([LEMMY] "Scale and zero position are
+fit together"; [AGI] "Fitting and runtime"; [ALPHA] bullets).
+
+Where the pages are silent the readings below are build decisions (bit order,
+reduction order, rounding of d, the starting pattern); each is stated at the
+function that makes it.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+against enumeration, exact rational arithmetic, closed forms or brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+QK = 256                 # weights per block                 [LEMMY] "Four weights, five bits"
+GROUP = 4                # weights per group                 [LEMMY] "Four weights, five bits"
+NGROUPS = QK // GROUP    # 64 groups per block
+BLOCK_BYTES = 42         # 2 (fp16 d) + 32 (4-bit codes) + 8 (select bits)   [ALPHA] "How STQ1_0 works"
+FP16_MAX = 65504.0
+
+
+# -----------------------------------------------------------------------------
+# O1: the 32-entry codebook
+# -----------------------------------------------------------------------------
+def pattern_of_code(c: int) -> tuple[int, int, int, int]:
+    """Ternary pattern (t0, t1, t2, t3) of code c in [0, 32).
+
+    Reading (the pages give no order): c = 8*z + m.  z = c >> 3 is the zero
+    lane; the three other lanes, taken in increasing lane order, get -1 when
+    their bit of m is set (lowest lane -> bit 0) and +1 otherwise.  The
+    "table select" bit (c >> 4) is therefore 1 exactly when the zero sits in
+    lanes 2..3, and the 4-bit code is c & 15.
+    """
+    if not 0 <= c < 32:
+        raise ValueError("code out of range")
+    z, m = c >> 3, c & 7
+    out, r = [], 0
+    for j in range(GROUP):
+        if j == z:
+            out.append(0)
+        else:
+            out.append(-1 if (m >> r) & 1 else 1)
+            r += 1
+    return tuple(out)
+
+
+CODEBOOK = np.array([pattern_of_code(c) for c in range(32)], dtype=np.int8)  # [32, 4]
+
+
+def codes_from_pattern(z: np.ndarray, neg: np.ndarray) -> np.ndarray:
+    """Inverse of the codebook for arrays: z [...] zero lane, neg [..., 4] sign flags.
+
+    The sign flag of the zero lane is ignored.
+    """
+    z = np.asarray(z, dtype=np.int64)
+    neg = np.asarray(neg, dtype=bool)
+    m = np.zeros(z.shape, dtype=np.int64)
+    for j in range(GROUP):
+        rank = j - (j > z).astype(np.int64)            # rank of lane j among the nonzero lanes
+        bit = neg[..., j] & (z != j)
+        m |= bit.astype(np.int64) << np.where(z != j, rank, 0)
+    return (8 * z + m).astype(np.uint8)
+
+
+# -----------------------------------------------------------------------------
+# O2: block byte layout
+# -----------------------------------------------------------------------------
+def qs_position(g: int) -> tuple[int, int]:
+    """(byte offset inside the block, bit shift) of the 4-bit code of group g.
+
+    Reading (the pages fix only the 42-byte total): bytes 2..33 hold the 64
+    four-bit codes.  Group g sits in byte 2 + 4*(g >> 3) + (g & 3), low nibble
+    when bit 2 of g is clear, high nibble otherwise.  So the 32-bit word w of
+    this field carries groups 8w..8w+7 and groups with equal g & 3 share a byte
+    lane.
+    """
+    return 2 + 4 * (g >> 3) + (g & 3), 4 * ((g >> 2) & 1)
+
+
+def qh_position(g: int) -> tuple[int, int]:
+    """(byte offset inside the block, bit index) of the select bit of group g.
+
+    Reading: bytes 34..41 hold the 64 select bits.  Group g's bit is bit
+    ((g >> 2) & 7) of byte 34 + 4*(g >> 5) + (g & 3): the same byte lane as its
+    code nibble, so the eight select bits for code word w sit at bits 2*(w&3)
+    and 2*(w&3)+1 of the four bytes of select word w >> 2.
+    """
+    return 34 + 4 * (g >> 5) + (g & 3), (g >> 2) & 7
+
+
+def pack_blocks(d16_bits: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """Pack fp16 scale bits [nb] and 5-bit codes [nb, 64] into blocks [nb, 42].
+
+    Bytes 0..1 hold d as IEEE binary16, little-endian.
+    """
+    d16_bits = np.asarray(d16_bits, dtype=np.uint16).reshape(-1)
+    codes = np.asarray(codes, dtype=np.uint8).reshape(-1, NGROUPS)
+    nb = codes.shape[0]
+    if d16_bits.shape[0] != nb:
+        raise ValueError("one scale per block")
+    if np.any(codes >= 32):
+        raise ValueError("codes are 5-bit")
+    out = np.zeros((nb, BLOCK_BYTES), dtype=np.uint8)
+    out[:, 0] = (d16_bits & 0xFF).astype(np.uint8)
+    out[:, 1] = (d16_bits >> 8).astype(np.uint8)
+    for g in range(NGROUPS):
+        byte, shift = qs_position(g)
+        out[:, byte] |= ((codes[:, g] & 15) << shift).astype(np.uint8)
+        byte, bit = qh_position(g)
+        out[:, byte] |= ((codes[:, g] >> 4) << bit).astype(np.uint8)
+    return out
+
+
+def unpack_blocks(raw: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Inverse of pack_blocks: blocks [nb, 42] -> (d16 bits [nb], codes [nb, 64])."""
+    raw = np.asarray(raw, dtype=np.uint8).reshape(-1, BLOCK_BYTES)
+    d16 = raw[:, 0].astype(np.uint16) | (raw[:, 1].astype(np.uint16) << 8)
+    codes = np.zeros((raw.shape[0], NGROUPS), dtype=np.uint8)
+    for g in range(NGROUPS):
+        byte, shift = qs_position(g)
+        nib = (raw[:, byte] >> shift) & 15
+        byte, bit = qh_position(g)
+        sel = (raw[:, byte] >> bit) & 1
+        codes[:, g] = nib | (sel << 4)
+    return d16, codes
+
+
+def row_bytes(k: int) -> int:
+    """Bytes of one packed row of k weights (k must be a multiple of 256)."""
+    if k % QK:
+        raise ValueError("k must be a multiple of 256")
+    return k // QK * BLOCK_BYTES
+
+
+# -----------------------------------------------------------------------------
+# O3: decode
+# -----------------------------------------------------------------------------
+def fp16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def dequantize_rows(q: np.ndarray, n_rows: int, k: int) -> np.ndarray:
+    """Packed rows [n_rows, k/256*42] -> fp32 weights [n_rows, k].
+
+    Each weight is its block's fp16 scale widened to fp32 times the pattern
+    value: +d, -d, or +0.0 in the zero lane ([LEMMY] "Four weights, five
+    bits").  The sign is applied by negation, so it is exact for every d.
+    """
+    q = np.asarray(q, dtype=np.uint8).reshape(n_rows, -1)
+    if q.shape[1] != row_bytes(k):
+        raise ValueError("row size does not match k")
+    d16, codes = unpack_blocks(q.reshape(-1, BLOCK_BYTES))
+    d = fp16_bits_to_f32(d16)[:, None, None]                    # [nb, 1, 1]
+    t = CODEBOOK[codes.astype(np.int64)]                         # [nb, 64, 4]
+    w = np.where(t > 0, d, np.negative(d))
+    w = np.where(t == 0, np.float32(0.0), w).astype(np.float32)
+    return w.reshape(n_rows, k)
+
+
+# -----------------------------------------------------------------------------
+# encoders (O4 amax baseline, O5 alternating WLS / zero choice)
+# -----------------------------------------------------------------------------
+def fp16_scale_bits(d: np.ndarray) -> np.ndarray:
+    """Round a non-negative fp64 scale to the stored fp16 bits.
+
+    Reading ([LEMMY] says only "FP16 scale"): fp64 -> fp32 with
+    round-to-nearest-even, clamp to the largest finite fp16 (65504), then
+    fp32 -> fp16 with round-to-nearest-even.  fp16 subnormals are kept.
+    """
+    f = np.asarray(d, dtype=np.float64).astype(np.float32)
+    f = np.minimum(f, np.float32(FP16_MAX))
+    return f.astype(np.float16).view(np.uint16)
+
+
+def _group_partial(v: np.ndarray) -> np.ndarray:
+    """Per-group sum of the 4 lanes, strictly in lane order: ((v0+v1)+v2)+v3."""
+    return ((v[..., 0] + v[..., 1]) + v[..., 2]) + v[..., 3]
+
+
+def _tree_sum(v: np.ndarray) -> np.ndarray:
+    """Sum of the last axis (length a power of two) as a balanced tree of
+    adjacent pairs: level 1 adds (0,1),(2,3),..., level 2 adds those pairs, ...
+
+    Reading: the pages do not fix a summation order; this fixed order makes
+    the encoder's result unique (it is the order of a 64-lane xor butterfly).
+    """
+    while v.shape[-1] > 1:
+        v = v[..., 0::2] + v[..., 1::2]
+    return v[..., 0]
+
+
+def wls_scale(absw: np.ndarray, q: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """Weighted-least-squares d for fixed zero lanes (signs follow w).
+
+    absw, q: fp64 [..., 64, 4]; z: int [..., 64].  With the zero lanes and the
+    signs fixed, the weighted error sum q_i (|w_i| - d)^2 over the nonzero
+    lanes is a quadratic in d whose minimiser is sum(q|w|) / sum(q)
+    ([LEMMY] "Scale and zero position are fit together": d is fit by weighted
+    least squares).  Reading: d = 0 when every nonzero lane has q = 0.
+    """
+    lane = np.arange(GROUP)
+    keep = lane != z[..., None]
+    num = _tree_sum(_group_partial(np.where(keep, q * absw, 0.0)))
+    den = _tree_sum(_group_partial(np.where(keep, q, 0.0)))
+    safe = np.where(den > 0.0, den, 1.0)
+    return np.where(den > 0.0, num / safe, 0.0)
+
+
+def choose_zero(absw: np.ndarray, q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Zero lane per group for a fixed scale d >= 0.
+
+    Zeroing lane j instead of keeping it at sign(w_j)*d raises the weighted
+    error by q_j*d*(2|w_j| - d); the lane with the least extra error is zeroed,
+    which need not be the smallest |w_j| ([LEMMY] "Scale and zero position are
+    fit together").  The common factor d >= 0 is dropped, ties go to the lowest
+    lane, cost = q_j * (2|w_j| - d) evaluated in fp64 in that operation order.
+    """
+    cost = q * (2.0 * absw - d[..., None, None])
+    return np.argmin(cost, axis=-1)
+
+
+def _blocks_view(w: np.ndarray, imatrix) -> tuple[np.ndarray, np.ndarray]:
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim != 2 or w.shape[1] % QK:
+        raise ValueError("w must be [n_rows, k] with k % 256 == 0")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weights are outside the contract")
+    n, k = w.shape
+    wb = w.reshape(n, k // QK, NGROUPS, GROUP)
+    if imatrix is None:
+        qb = np.ones_like(wb)
+    else:
+        qv = np.asarray(imatrix, dtype=np.float32).reshape(-1)
+        if qv.shape[0] != k or not np.all(np.isfinite(qv)) or np.any(qv < 0):
+            raise ValueError("imatrix must be k finite non-negative values")
+        qb = np.broadcast_to(qv.reshape(1, k // QK, NGROUPS, GROUP), wb.shape)
+    return wb, qb
+
+
+def encode_trace(w: np.ndarray, imatrix=None, rounds: int = 3) -> dict:
+    """Run the WLS encoder and keep every intermediate (for the round tests).
+
+    Order (reading of "alternates ... three alternating rounds", [LEMMY]):
+      p0 = amax pattern (zero the smallest |w| of each group, signs of w);
+      repeat `rounds` times: d <- WLS(p), p <- choose(d);
+      finally d <- WLS(p) so the stored d fits the stored pattern.
+    Returns fp64 arrays: 'absw','q' [n,nb,64,4], 'neg' bool, and lists
+    'z' (rounds+1 patterns) and 'd' (rounds+1 scales, d[r] = WLS(z[r])).
+    """
+    wb, qb = _blocks_view(w, imatrix)
+    absw = np.abs(wb.astype(np.float64))
+    q = qb.astype(np.float64)
+    neg = wb < 0                                   # -0.0 counts as positive
+    z = np.argmin(absw, axis=-1)                   # p0: first smallest |w|
+    zs, ds = [z], []
+    for _ in range(rounds):
+        d = wls_scale(absw, q, z)
+        ds.append(d)
+        z = choose_zero(absw, q, d)
+        zs.append(z)
+    ds.append(wls_scale(absw, q, z))
+    return {"absw": absw, "q": q, "neg": neg, "z": zs, "d": ds}
+
+
+def quantize_rows(w: np.ndarray, imatrix=None, encoder: str = "wls", rounds: int = 3) -> np.ndarray:
+    """Encode fp32 rows [n, k] into packed STQ1_0 rows [n, k/256*42] (uint8).
+
+    encoder='wls'  : alternating WLS scale / weighted zero choice (O5), `rounds` rounds.
+    encoder='amax' : the original ternary encoder ([ALPHA] bullets: it used
+                     amax scaling): d = max|w| of the block, zero the smallest
+                     |w| of each group (first on ties), signs of w.  `rounds`
+                     is ignored.
+    A missing imatrix means q = 1 for every column.
+    """
+    wb, _ = _blocks_view(w, imatrix)
+    n, nb = wb.shape[0], wb.shape[1]
+    neg = wb < 0
+    if encoder == "amax":
+        absw = np.abs(wb.astype(np.float64))
+        z = np.argmin(absw, axis=-1)
+        d = absw.reshape(n, nb, QK).max(axis=-1)
+    elif encoder == "wls":
+        if rounds < 0:
+            raise ValueError("rounds must be >= 0")
+        tr = encode_trace(w, imatrix, rounds)
+        z, d = tr["z"][-1], tr["d"][-1]
+    else:
+        raise ValueError("encoder must be 'wls' or 'amax'")
+    codes = codes_from_pattern(z, neg)
+    packed = pack_blocks(fp16_scale_bits(d).reshape(-1), codes.reshape(-1, NGROUPS))
+    return packed.reshape(n, nb * BLOCK_BYTES)
+
+
+# -----------------------------------------------------------------------------
+# O6: weighted reconstruction error
+# -----------------------------------------------------------------------------
+def weighted_error(w: np.ndarray, w_hat: np.ndarray, imatrix=None, axis=None):
+    """E = sum_i q_i (w_i - w_hat_i)^2 in fp64 (q = 1 when imatrix is None)."""
+    w = np.asarray(w, dtype=np.float64)
+    diff = w - np.asarray(w_hat, dtype=np.float64)
+    q = np.ones(w.shape[-1]) if imatrix is None else np.asarray(imatrix, dtype=np.float64)
+    return np.sum(q * diff * diff, axis=axis)
+
+
+def pattern_error(absw, q, z, d) -> np.ndarray:
+    """Per-block weighted error of pattern z (signs of w) with scale d (fp64)."""
+    lane = np.arange(GROUP)
+    zero = lane == z[..., None]
+    err = np.where(zero, absw, absw - d[..., None, None])
+    return np.sum(q * err * err, axis=(-1, -2))
+
+
+# -----------------------------------------------------------------------------
+# O7 / O8: products
+# -----------------------------------------------------------------------------
+def gemv(q: np.ndarray, n_rows: int, k: int, x: np.ndarray) -> np.ndarray:
+    """y = W_hat x in fp64.  Each product fp32 x (bf16 or fp32) is exact in
+    fp64; the fp64 dot adds relative error ~1e-16, far inside any tolerance."""
+    w_hat = dequantize_rows(q, n_rows, k).astype(np.float64)
+    return w_hat @ np.asarray(x, dtype=np.float64).reshape(k)
+
+
+def gemv_tokens(q: np.ndarray, n_rows: int, k: int, x: np.ndarray) -> np.ndarray:
+    """Y[t, n] = sum_k W_hat[n, k] x[t, k] for several tokens x [T, k] (fp64)."""
+    w_hat = dequantize_rows(q, n_rows, k).astype(np.float64)
+    return np.asarray(x, dtype=np.float64).reshape(-1, k) @ w_hat.T
+
+
+def grouped_gemm(table: np.ndarray, expert_stride: int, n_rows: int, k: int,
+                 x_sorted: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """Per expert e: Y[off[e]:off[e+1]] = X[off[e]:off[e+1]] @ W_hat_e^T (fp64)."""
+    table = np.asarray(table, dtype=np.uint8).reshape(-1)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    x = np.asarray(x_sorted, dtype=np.float64).reshape(-1, k)
+    y = np.zeros((x.shape[0], n_rows), dtype=np.float64)
+    rb = row_bytes(k)
+    for e in range(offsets.shape[0] - 1):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi <= lo:
+            continue
+        raw = table[e * expert_stride: e * expert_stride + n_rows * rb]
+        y[lo:hi] = x[lo:hi] @ dequantize_rows(raw, n_rows, k).astype(np.float64).T
+    return y
+
+
+def tolerance_scale(q: np.ndarray, n_rows: int, k: int, x: np.ndarray) -> np.ndarray:
+    """A[t, n] = sum_b d_{n,b} * sum_{k in block b} |x[t, k]| (fp64), the scale
+    of the per-element error bound for row n and token t."""
+    d16, _ = unpack_blocks(np.asarray(q, dtype=np.uint8).reshape(-1, BLOCK_BYTES))
+    d = np.abs(fp16_bits_to_f32(d16).astype(np.float64)).reshape(n_rows, k // QK)
+    ax = np.abs(np.asarray(x, dtype=np.float64).reshape(-1, k // QK, QK)).sum(axis=-1)
+    return ax @ d.T
