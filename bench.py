@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the STQ1_0 sparse-ternary matmul on one MI355X.
+
+One step is one pass of the hot path over one batch of synthetic input:
+  * decode: the gathered GEMV of a 256-expert MoE layer (gate+up, 4096 x 7168
+    per expert, 1.23 GB packed) at batch 1, 4, 16 and 64 tokens with fresh
+    uniform top-8 routing, on the WLS-encoded table and on an amax-encoded
+    table of the same weights (kernel speed must not depend on the encoder);
+  * prefill: the grouped GEMM of 2048 tokens routed top-8 (16384 rows grouped
+    by expert) against the same table.
+Inputs are resident in HBM before timing starts.  `value` is the GEMV's
+effective bandwidth over the sweep: algorithmic bytes (each touched expert's
+packed bytes once, plus activations and outputs) divided by GEMV time.
+Kernel durations come from HIP events recorded on the launch stream.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--single-expert]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+BATCHES = (1, 4, 16, 64)
+PREFILL_TOKENS = 2048
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "sparse_ternary_bit_amd", "csrc", name)
+    h = hashlib.sha256()
+    for f in (p, os.path.join(ROOT, "sparse_ternary_bit_amd", "csrc", "stq_device.hpp")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_file: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_file)
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel_file):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(seconds: float):
+    """The oracle's GEMV, as it stands, on a bounded sample of the decode
+    workload: 512 rows of one expert (the oracle encodes them itself), one
+    token, repeated for about `seconds`."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import stq_workloads as W
+    import synth_inputs as S
+    from oracle import stq_oracle as O
+
+    rows = np.arange(512)
+    w = W.expert_weight_rows(W.TABLE_SEED, 0, rows)
+    q = S.calibration_imatrix(W.IMATRIX_SEED, 64, W.K)
+    packed = O.quantize_rows(w, q)
+    xb, xf = S.bf16_normal(np.random.default_rng(4000), (1, W.K))
+    nbytes = packed.nbytes + W.K * 2 + len(rows) * 4
+    with threadpool_limits(limits=1):
+        O.gemv(packed, len(rows), W.K, xf[0])                # warm
+        t0 = time.perf_counter()
+        calls = 0
+        while time.perf_counter() - t0 < seconds:
+            O.gemv(packed, len(rows), W.K, xf[0])
+            calls += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(nbytes * calls / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle GEMV (decode + fp64 dot) of 512 rows x 7168 of one expert, one bf16 token, "
+                      f"{calls} calls in {dt:.1f} s; same algorithmic-byte count as the GPU figure"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--single-expert", action="store_true",
+                    help="also time the batch-1 single-expert GEMV over 100 resident experts")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the STQ1_0 path here has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_ternary_bit_amd as stq
+    import stq_workloads as W
+    import synth_inputs as S
+
+    if not os.path.exists(stq.lib_path()):
+        from sparse_ternary_bit_amd import build as _b
+        _b.build(verbose=False)
+    stq.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N, K, E = W.N_ROWS, W.K, W.N_EXPERTS
+    rb = stq.row_bytes(K)
+    expert_bytes = N * rb
+
+    # ---------------- setup (untimed) ----------------
+    q = W.table_imatrix(device=dev)
+    t_wls, stride = W.encode_table(imatrix=q, encoder=stq.ENC_WLS, device=dev)
+    t_amax, _ = W.encode_table(imatrix=q, encoder=stq.ENC_AMAX, device=dev)
+    tables = {"wls": t_wls, "amax": t_amax}
+
+    total_steps = args.warmup + args.steps
+    sweep = []   # per step: list of (batch, pe, pt, x, y, algorithmic bytes)
+    for s in range(total_steps):
+        items = []
+        for B in BATCHES:
+            pe_t, pt_t, pe, pt = W.decode_pairs(50000 + 1000 * s + B, B, device=dev)
+            x = S.torch_bf16_normal(90000 + 1000 * s + B, (B, K), device=dev)
+            y = torch.empty((B * W.TOP_K, N), dtype=torch.float32, device=dev)
+            uniq = len(np.unique(pe))
+            nbytes = uniq * expert_bytes + B * K * 2 + B * W.TOP_K * N * 4
+            items.append((B, pe_t, pt_t, x, y, nbytes, uniq))
+        sweep.append(items)
+    x_sorted, offsets_t, _, offsets = W.prefill_batch(PREFILL_TOKENS, K, device=dev)
+    total_m = int(offsets[-1])
+    y_pre = torch.empty((total_m, N), dtype=torch.float32, device=dev)
+    gemm_flop = 2.0 * total_m * N * K
+
+    if args.single_expert:
+        xs1 = [S.torch_bf16_normal(4000 + i, (1, K), device=dev) for i in range(100)]
+        pes1 = [torch.tensor([i], dtype=torch.int32, device=dev) for i in range(100)]
+        ys1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def run_step(s, rec):
+        for enc in ("wls", "amax"):
+            for (B, pe_t, pt_t, x, y, nbytes, uniq) in sweep[s]:
+                a, b = ev(), ev()
+                a.record(stream)
+                stq.gemv(tables[enc], stride, E, N, K, x, pe_t, pt_t, out=y)
+                b.record(stream)
+                rec["gemv"].append((enc, B, nbytes, uniq, a, b))
+        a, b = ev(), ev()
+        a.record(stream)
+        stq.grouped_gemm(t_wls, stride, E, N, K, x_sorted, offsets_t, out=y_pre)
+        b.record(stream)
+        rec["gemm"].append((a, b))
+        if args.single_expert:
+            for i in range(100):
+                a, b = ev(), ev()
+                a.record(stream)
+                stq.gemv(t_wls, stride, E, N, K, xs1[i], pes1[i], out=ys1)
+                b.record(stream)
+                rec["single"].append((a, b))
+
+    for s in range(args.warmup):
+        run_step(s, {"gemv": [], "gemm": [], "single": []})
+    torch.cuda.synchronize()
+
+    rec = {"gemv": [], "gemm": [], "single": []}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        run_step(s, rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # ---------------- results ----------------
+    gemv_ms = [a.elapsed_time(b) for (_, _, _, _, a, b) in rec["gemv"]]
+    gemv_bytes = [nb for (_, _, nb, _, _, _) in rec["gemv"]]
+    tot_b, tot_ms = float(sum(gemv_bytes)), float(sum(gemv_ms))
+    gemv_gbs = tot_b / (tot_ms * 1e-3) / 1e9
+    per_batch = {}
+    for enc in ("wls", "amax"):
+        for B in BATCHES:
+            sel = [(nb, ms, u) for (e_, b_, nb, u, _, _), ms in zip(rec["gemv"], gemv_ms) if e_ == enc and b_ == B]
+            bb = sum(x[0] for x in sel)
+            mm = sum(x[1] for x in sel)
+            per_batch[f"{enc}_b{B}"] = {"GB/s": round(bb / (mm * 1e-3) / 1e9, 1),
+                                        "us": round(1e3 * mm / len(sel), 2),
+                                        "experts": round(sum(x[2] for x in sel) / len(sel), 1)}
+    gemm_ms = [a.elapsed_time(b) for (a, b) in rec["gemm"]]
+    gemm_avg = float(np.mean(gemm_ms))
+    gemm_tflops = gemm_flop / (gemm_avg * 1e-3) / 1e12
+
+    n_launch = len(gemv_ms)
+    traffic = measured_traffic("k_gemv.hip")
+    traffic_gemm = measured_traffic("k_gemm.hip")
+    out = {
+        "metric": "STQ1_0 expert GEMV HBM GB/s (% peak); prefill grouped-GEMM TFLOP/s (% peak)",
+        "value": round(gemv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "moe_layer_sweep_and_prefill", "experts": E, "n": N, "k": K,
+                   "top_k": W.TOP_K, "decode_batches": list(BATCHES), "decode_tables": ["wls", "amax"],
+                   "prefill_tokens": PREFILL_TOKENS, "prefill_rows": total_m,
+                   "weights": "iid N(0,0.02) fp32 encoded to STQ1_0 (42 B / 256)",
+                   "activations": "bf16 N(0,1)"},
+        "roofline": {"bound": "hbm", "achieved": round(tot_b / n_launch / (tot_ms / n_launch * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "gemv_kernel (stq_gemv)",
+                     "algorithmic_bytes_per_launch": round(tot_b / n_launch),
+                     "avg_launch_us": round(1e3 * tot_ms / n_launch, 2)},
+        "roofline_gemm": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+                          "traffic": traffic_gemm, "kernel": "grouped_gemm_kernel (stq_grouped_gemm)",
+                          "flop_per_launch": gemm_flop, "avg_launch_us": round(1e3 * gemm_avg, 1)},
+        "gemv_sweep": per_batch,
+    }
+    if rec["single"]:
+        sm = [a.elapsed_time(b) for (a, b) in rec["single"]]
+        sb = expert_bytes + K * 2 + N * 4
+        out["single_expert_gemv"] = {"us_median": round(1e3 * float(np.median(sm)), 2),
+                                     "us_p10": round(1e3 * float(np.percentile(sm, 10)), 2),
+                                     "us_p90": round(1e3 * float(np.percentile(sm, 90)), 2),
+                                     "GB/s_median": round(sb / (float(np.median(sm)) * 1e-3) / 1e9, 1)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,152 @@
+/*
+ * stq.h -- C ABI of libstq, the STQ1_0 sparse-ternary quantized matmul for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * STQ1_0 (sources named by page title / address and section):
+ *   - every group of four consecutive weights holds values in {-d, 0, +d} with
+ *     exactly one zero lane: 4 zero positions x 8 sign choices = 32 patterns,
+ *     five bits per group (lemmy.durstig.online post 66506, paragraph "Four
+ *     weights, five bits");
+ *   - the five bits are a 4-bit code plus a 1-bit table select into a
+ *     32-entry codebook, one fp16 scale d is shared by 256 weights, and a block
+ *     of 256 weights takes 42 bytes, 1.3125 bits per weight (alphasignal.ai,
+ *     "AngelSlim Shrinks Tencent's 1.5TB Hy4-Preview ...", section "How STQ1_0
+ *     works").
+ *
+ * Block layout (this library's definition; the pages fix only the size):
+ *   bytes  0..1   d, IEEE binary16, little-endian
+ *   bytes  2..33  4-bit codes: group g (0..63) in byte 2 + 4*(g>>3) + (g&3),
+ *                 low nibble when bit 2 of g is clear, high nibble otherwise
+ *   bytes 34..41  select bits: group g's bit is bit ((g>>2)&7) of byte
+ *                 34 + 4*(g>>5) + (g&3)
+ *   code c = nibble | select<<4;  zero lane z = c>>3;  m = c&7; the three
+ *   other lanes in increasing order take -1 when their bit of m is set
+ *   (lowest lane -> bit 0), else +1.  Decoded weight = +/-fp32(d), or +0.0
+ *   in the zero lane.
+ * A packed row of k weights (k a multiple of 256) is k/256 consecutive
+ * blocks, block b covering columns 256b..256b+255; a packed matrix is rows
+ * back to back, row_bytes = k/256*42 apart.
+ *
+ * Conventions for every entry point:
+ *   - array arguments are DEVICE pointers owned by the caller, unless stated;
+ *   - work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *     no entry point synchronises the host;
+ *   - arguments are validated on the host before any launch; a failed check
+ *     returns a status and stq_last_error() holds a message (thread-local);
+ *   - STQ_E_HIP means a HIP call failed (launch, allocation); device faults
+ *     surface at the caller's next synchronisation;
+ *   - stq_gemv keeps a per-device scratch buffer that it grows on demand with
+ *     hipMalloc and keeps until the process ends (see stq_gemv).
+ */
+#ifndef STQ_H
+#define STQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* stq_stream_t; /* same object as a hipStream_t */
+
+#define STQ_QK 256          /* weights per block */
+#define STQ_BLOCK_BYTES 42  /* bytes per block   */
+
+typedef enum {
+  STQ_OK = 0,
+  STQ_E_ARG = 1,   /* null pointer, bad enum, negative count               */
+  STQ_E_SHAPE = 2, /* k not a multiple of 256, sizes inconsistent           */
+  STQ_E_ALIGN = 3, /* pointer or stride misaligned                          */
+  STQ_E_HIP = 4    /* a HIP runtime call failed                             */
+} stq_status;
+
+enum { STQ_ENC_WLS = 0, STQ_ENC_AMAX = 1 };
+enum { STQ_X_F32 = 0, STQ_X_BF16 = 1 };
+
+/* Bytes of one packed row of k weights: k/256*42, or -1 if k is not a
+ * positive multiple of 256. Pure host function. */
+int64_t stq_row_bytes(int64_t k);
+
+/* Encode fp32 rows into STQ1_0 (weighted least squares scale alternating
+ * with an importance-weighted choice of the zero lane; lemmy post 66506,
+ * paragraph "Scale and zero position are fit together"; amax baseline from
+ * the alphasignal.ai summary bullets).
+ *   w        [n_rows, k] fp32, row-major, 4-byte aligned, finite values
+ *   imatrix  [k] fp32 >= 0, per-column importance; NULL means all ones
+ *   encoder  STQ_ENC_WLS: start from the amax pattern (zero the smallest |w|
+ *              of each group, signs of w); `rounds` times fit d by weighted
+ *              least squares then re-choose every group's zero lane by least
+ *              added weighted error q_j*(2|w_j|-d) (lowest lane on ties);
+ *              a final fit gives the stored d.
+ *            STQ_ENC_AMAX: d = block max |w|, smallest |w| zeroed; `rounds`
+ *              ignored.
+ *   rounds   >= 0 (3 is the pages' setting)
+ *   out      [n_rows, k/256*42] bytes
+ * Sums run in fp64 in a fixed order (lanes of a group in order, then a
+ * balanced tree of adjacent groups); d is stored as fp16 via fp32
+ * (round-to-nearest-even both times, clamped to 65504).  The result is
+ * bit-identical to the reference encoder.  Non-finite inputs are outside
+ * the contract (output unspecified). */
+stq_status stq_quantize_rows(const float* w, const float* imatrix, int64_t n_rows, int64_t k,
+                             int encoder, int rounds, uint8_t* out, stq_stream_t stream);
+
+/* Decode packed rows to fp32: out[r, i] = +/-fp32(d) or +0.0 (bit-exact).
+ *   q    [n_rows, k/256*42] bytes, 2-byte aligned
+ *   out  [n_rows, k] fp32 */
+stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, float* out,
+                               stq_stream_t stream);
+
+/* Gathered decode GEMV over (token, expert) pairs, the STQ1_0 matmul of the
+ * decode path (lemmy post 66506, paragraph "Runtime": STQ1_0 kernels run the
+ * expert projections).
+ *   w_table   expert e's packed [n, k] matrix starts at w_table + e*expert_stride_bytes;
+ *             w_table 16-byte aligned, expert_stride_bytes a multiple of 16 and
+ *             >= n*row_bytes(k)
+ *   x         activations [n_tokens, k] with row stride x_row_stride elements,
+ *             fp32 (STQ_X_F32, 4-byte aligned) or bf16 bits (STQ_X_BF16,
+ *             x_row_stride even, 4-byte aligned rows)
+ *   pair_expert, pair_token  int32 [n_pairs]; pair i computes
+ *             y[i, :] = W_{pair_expert[i]} x[pair_token[i], :].
+ *             NULL pair_expert means expert 0 for every pair; NULL pair_token
+ *             means token i for pair i.  Pairs sharing an expert are batched so
+ *             the expert's weights stream once per call.  A pair whose expert
+ *             is outside [0, n_experts) or whose token is outside
+ *             [0, n_tokens) gets a row of NaN.
+ *   y         [n_pairs, n] fp32
+ * Accumulation is fp32 with products exact; the summation order is fixed,
+ * so repeated calls give identical bits.  Splitting k across workgroups uses
+ * a per-device scratch buffer (grown with hipMalloc on first need and kept);
+ * calls that overlap on one device must use the same stream. */
+stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts,
+                    int64_t n, int64_t k, const void* x, int x_dtype, int64_t x_row_stride,
+                    int64_t n_tokens, const int32_t* pair_expert, const int32_t* pair_token,
+                    int64_t n_pairs, float* y, stq_stream_t stream);
+
+/* Grouped GEMM of the prefill path: tokens routed to each expert,
+ * grouped by expert, times that expert's STQ1_0 matrix.
+ *   x_sorted        [total_m, k] bf16 bits, row-major, 16-byte aligned rows
+ *                   (k*2 bytes apart)
+ *   expert_offsets  DEVICE int32 [n_experts+1], non-decreasing, offsets[0] = 0,
+ *                   offsets[n_experts] = total_m: rows offsets[e]..offsets[e+1]-1
+ *                   belong to expert e
+ *   y               [total_m, n] fp32: y[r, :] = W_e x_sorted[r, :]
+ * bf16 x ternary products on matrix cores (exact), fp32 accumulation, one
+ * fp32 multiply by d per 256-weight block.  Offsets that break the stated
+ * invariants are outside the contract (rows may be skipped). */
+stq_status stq_grouped_gemm(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts,
+                            int64_t n, int64_t k, const uint16_t* x_sorted,
+                            const int32_t* expert_offsets, int64_t total_m, float* y,
+                            stq_stream_t stream);
+
+/* Static text of a status code. */
+const char* stq_status_string(stq_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* stq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STQ_H */

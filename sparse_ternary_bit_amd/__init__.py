@@ -1,0 +1,179 @@
+"""Python binding of libstq, the STQ1_0 sparse-ternary matmul library for MI355X.
+
+Thin ctypes marshalling over the C ABI in ``include/stq.h``: every function
+takes torch tensors that already live on the GPU, passes their device
+pointers and the current HIP stream, and checks the returned status.  All
+computation happens in the HIP kernels of ``libstq.so``; there is no
+fallback.  If the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "QK", "BLOCK_BYTES", "ENC_WLS", "ENC_AMAX", "StqError", "lib", "lib_path",
+    "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "grouped_gemm",
+]
+
+QK = 256
+BLOCK_BYTES = 42
+ENC_WLS, ENC_AMAX = 0, 1
+X_F32, X_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libstq.so")
+_lib = None
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_vp = ctypes.c_void_p
+
+
+class StqError(RuntimeError):
+    """A libstq entry point returned a status other than STQ_OK."""
+
+    def __init__(self, func: str, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{func} failed with status {status}: {detail}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libstq.so (built in-tree by ``python -m sparse_ternary_bit_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m sparse_ternary_bit_amd.build` first")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.stq_row_bytes.argtypes = [_c_i64]
+    L.stq_row_bytes.restype = _c_i64
+    L.stq_status_string.argtypes = [_c_int]
+    L.stq_status_string.restype = ctypes.c_char_p
+    L.stq_last_error.argtypes = []
+    L.stq_last_error.restype = ctypes.c_char_p
+    L.stq_quantize_rows.argtypes = [_c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp]
+    L.stq_quantize_rows.restype = _c_int
+    L.stq_dequantize_rows.argtypes = [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]
+    L.stq_dequantize_rows.restype = _c_int
+    L.stq_gemv.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_i64, _c_i64,
+                           _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
+    L.stq_gemv.restype = _c_int
+    L.stq_grouped_gemm.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
+    L.stq_grouped_gemm.restype = _c_int
+    _lib = L
+    return L
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise StqError(func, status, lib().stq_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _on_gpu(name: str, t: torch.Tensor, dtype: torch.dtype) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def row_bytes(k: int) -> int:
+    rb = lib().stq_row_bytes(int(k))
+    if rb < 0:
+        raise ValueError("k must be a positive multiple of 256")
+    return rb
+
+
+def quantize_rows(w: torch.Tensor, imatrix: torch.Tensor | None = None, encoder: int = ENC_WLS,
+                  rounds: int = 3, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Encode fp32 rows [n, k] on the GPU; returns uint8 [n, k/256*42]."""
+    _on_gpu("w", w, torch.float32)
+    n, k = w.shape
+    if imatrix is not None:
+        _on_gpu("imatrix", imatrix, torch.float32)
+    if out is None:
+        out = torch.empty((n, row_bytes(k)), dtype=torch.uint8, device=w.device)
+    _on_gpu("out", out, torch.uint8)
+    _check("stq_quantize_rows", lib().stq_quantize_rows(w.data_ptr(), _ptr(imatrix), n, k, int(encoder),
+                                                        int(rounds), out.data_ptr(), _stream()))
+    return out
+
+
+def dequantize_rows(q: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode packed rows to fp32 [n, k]."""
+    _on_gpu("q", q, torch.uint8)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=q.device)
+    _on_gpu("out", out, torch.float32)
+    _check("stq_dequantize_rows", lib().stq_dequantize_rows(q.data_ptr(), n, k, out.data_ptr(), _stream()))
+    return out
+
+
+def gemv(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: int, k: int, x: torch.Tensor,
+         pair_expert: torch.Tensor | None = None, pair_token: torch.Tensor | None = None,
+         n_pairs: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[i] = W_{pair_expert[i]} x[pair_token[i]] for every pair; x is [n_tokens, k] fp32 or bf16."""
+    _on_gpu("w_table", w_table, torch.uint8)
+    if x.dtype == torch.bfloat16:
+        xd = X_BF16
+    elif x.dtype == torch.float32:
+        xd = X_F32
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    _on_gpu("x", x, x.dtype)
+    n_tokens = x.shape[0]
+    if n_pairs is None:
+        if pair_expert is not None:
+            n_pairs = pair_expert.numel()
+        elif pair_token is not None:
+            n_pairs = pair_token.numel()
+        else:
+            n_pairs = n_tokens
+    for nm, t in (("pair_expert", pair_expert), ("pair_token", pair_token)):
+        if t is not None:
+            _on_gpu(nm, t, torch.int32)
+            if t.numel() != n_pairs:
+                raise ValueError(f"{nm} must hold n_pairs entries")
+    if out is None:
+        out = torch.empty((n_pairs, n), dtype=torch.float32, device=x.device)
+    _on_gpu("out", out, torch.float32)
+    # a one-row view may carry any stride in its first dimension; its rows are k apart
+    x_stride = x.stride(0) if n_tokens > 1 else x.shape[1]
+    _check("stq_gemv", lib().stq_gemv(w_table.data_ptr(), int(expert_stride), int(n_experts), int(n), int(k),
+                                      x.data_ptr(), xd, x_stride, n_tokens, _ptr(pair_expert),
+                                      _ptr(pair_token), int(n_pairs), out.data_ptr(), _stream()))
+    return out
+
+
+def grouped_gemm(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: int, k: int,
+                 x_sorted: torch.Tensor, offsets: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[rows of e] = X[rows of e] W_e^T with rows grouped by expert; x_sorted bf16 [total_m, k]."""
+    _on_gpu("w_table", w_table, torch.uint8)
+    _on_gpu("x_sorted", x_sorted, torch.bfloat16)
+    _on_gpu("offsets", offsets, torch.int32)
+    if offsets.numel() != n_experts + 1:
+        raise ValueError("offsets must hold n_experts + 1 entries")
+    total_m = x_sorted.shape[0]
+    if out is None:
+        out = torch.empty((total_m, n), dtype=torch.float32, device=x_sorted.device)
+    _on_gpu("out", out, torch.float32)
+    _check("stq_grouped_gemm", lib().stq_grouped_gemm(w_table.data_ptr(), int(expert_stride), int(n_experts),
+                                                      int(n), int(k), x_sorted.data_ptr(), offsets.data_ptr(),
+                                                      total_m, out.data_ptr(), _stream()))
+    return out

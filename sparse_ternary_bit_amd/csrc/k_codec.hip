@@ -1,0 +1,194 @@
+// STQ1_0 encode and decode kernels for gfx950.
+//
+// Encoder (lemmy.durstig.online post 66506, "Scale and zero position are fit
+// together"; alphasignal.ai summary bullets for the amax baseline): one
+// wavefront per 256-weight block, one lane per group of four.  All encoder
+// arithmetic is fp64 in a fixed order so the bytes match the reference
+// encoder exactly:
+//   - per group, the four lanes are added in lane order, a zeroed lane adding
+//     +0.0;
+//   - across the 64 groups, an xor butterfly over strides 1, 2, ..., 32, which
+//     is the balanced tree of adjacent pairs (floating-point addition is
+//     commutative, so every lane ends with the same bits);
+//   - q*|w| of two fp32 values is exact in fp64, so contraction cannot change
+//     it; the file is still built without contraction.
+// d is stored as fp16 by fp64 -> fp32 -> fp16, round-to-nearest-even each
+// time, clamped to 65504.
+#include "stq_device.hpp"
+#include "stq_launch.hpp"
+
+namespace stq {
+namespace {
+
+// ---------------------------------------------------------------------------
+// decode: one thread per group of four weights
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ q, int64_t n_groups,
+                                                         float* __restrict__ out) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= n_groups) return;
+  const int64_t blk = gid >> 6;
+  const int g = static_cast<int>(gid & 63);
+  const uint8_t* p = q + blk * kBlockBytes;
+  const uint32_t d16 = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8);
+  const uint32_t nib = (p[2 + 4 * (g >> 3) + (g & 3)] >> (4 * ((g >> 2) & 1))) & 15u;
+  const uint32_t sel = (p[34 + 4 * (g >> 5) + (g & 3)] >> ((g >> 2) & 7)) & 1u;
+  const uint32_t c = nib | (sel << 4);
+  const uint32_t dbits = __float_as_uint(half_bits_to_float(d16));
+  float* o = out + blk * kQK + 4 * g;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = code_lane_value(c, j);
+    o[j] = __uint_as_float(t == 0 ? 0u : (t < 0 ? (dbits ^ 0x80000000u) : dbits));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// encode: one wavefront per block
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_tree_sum(double v) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) v = v + __shfl_xor(v, s, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wls_scale(const double (&a)[4], const double (&q)[4], int z) {
+  // weighted least squares scale for fixed zero lanes: sum(q|w|) / sum(q) over kept lanes
+  double num = 0.0, den = 0.0;
+  {
+    const double n0 = (z == 0) ? 0.0 : q[0] * a[0];
+    const double n1 = (z == 1) ? 0.0 : q[1] * a[1];
+    const double n2 = (z == 2) ? 0.0 : q[2] * a[2];
+    const double n3 = (z == 3) ? 0.0 : q[3] * a[3];
+    num = ((n0 + n1) + n2) + n3;
+    const double d0 = (z == 0) ? 0.0 : q[0];
+    const double d1 = (z == 1) ? 0.0 : q[1];
+    const double d2 = (z == 2) ? 0.0 : q[2];
+    const double d3 = (z == 3) ? 0.0 : q[3];
+    den = ((d0 + d1) + d2) + d3;
+  }
+  num = wave_tree_sum(num);
+  den = wave_tree_sum(den);
+  return den > 0.0 ? num / den : 0.0;
+}
+
+__device__ __forceinline__ int choose_zero(const double (&a)[4], const double (&q)[4], double d) {
+  // zeroing lane j adds q_j * d * (2|w_j| - d) of weighted error; drop d >= 0
+  int z = 0;
+  double best = q[0] * (2.0 * a[0] - d);
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    const double c = q[j] * (2.0 * a[j] - d);
+    if (c < best) {
+      best = c;
+      z = j;
+    }
+  }
+  return z;
+}
+
+template <bool kWls>
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, const float* __restrict__ imat,
+                                                       int64_t n_blocks, int nb, int64_t k, int rounds,
+                                                       uint8_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (blk >= n_blocks) return;  // uniform per wavefront
+  const int64_t row = blk / nb;
+  const int b = static_cast<int>(blk - row * nb);
+  const int64_t col = static_cast<int64_t>(b) * kQK + 4 * lane;
+  const float* wp = w + row * k + col;
+
+  double a[4], q[4];
+  bool neg[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float v = wp[j];
+    a[j] = fabs(static_cast<double>(v));
+    neg[j] = v < 0.0f;  // -0.0 counts as positive
+    q[j] = imat ? static_cast<double>(imat[col + j]) : 1.0;
+  }
+  // starting pattern: zero the first smallest |w| of the group
+  int z = 0;
+#pragma unroll
+  for (int j = 1; j < 4; ++j)
+    if (a[j] < a[z]) z = j;
+
+  double d;
+  if (kWls) {
+    for (int r = 0; r < rounds; ++r) {
+      d = wls_scale(a, q, z);
+      z = choose_zero(a, q, d);
+    }
+    d = wls_scale(a, q, z);
+  } else {
+    d = fmax(fmax(a[0], a[1]), fmax(a[2], a[3]));
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) d = fmax(d, __shfl_xor(d, s, 64));
+  }
+
+  // fp16 scale: fp64 -> fp32 -> fp16, nearest-even each time, clamped to 65504
+  float f = static_cast<float>(d);
+  f = fminf(f, 65504.0f);
+  const uint32_t d16 = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+
+  // code = 8*z + m, m's bit r set when the r-th kept lane is negative
+  uint32_t m = 0;
+  int r = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j == z) continue;
+    m |= static_cast<uint32_t>(neg[j]) << r;
+    ++r;
+  }
+  const uint32_t c = 8u * static_cast<uint32_t>(z) + m;
+
+  // pack: code words (8 groups each) and select words (32 groups each)
+  const int g = lane;
+  uint32_t qsw = (c & 15u) << (8 * (g & 3) + 4 * ((g >> 2) & 1));
+  uint32_t qhw = (c >> 4) << (8 * (g & 3) + ((g >> 2) & 7));
+#pragma unroll
+  for (int s = 1; s < 8; s <<= 1) qsw |= __shfl_xor(qsw, s, 64);
+#pragma unroll
+  for (int s = 1; s < 32; s <<= 1) qhw |= __shfl_xor(qhw, s, 64);
+
+  // 21 half-words per block: [d | 16 x code half-words | 4 x select half-words]
+  const int i = lane;
+  int src = 0;
+  if (i >= 1 && i <= 16) src = 8 * ((i - 1) >> 1);
+  else if (i >= 17 && i <= 20) src = 32 * ((i - 17) >> 1);
+  const uint32_t vq = __shfl(qsw, src, 64);
+  const uint32_t vh = __shfl(qhw, src, 64);
+  uint32_t val;
+  if (i == 0) val = d16;
+  else if (i <= 16) val = (vq >> (16 * ((i - 1) & 1))) & 0xFFFFu;
+  else val = (vh >> (16 * ((i - 17) & 1))) & 0xFFFFu;
+  if (i < 21) reinterpret_cast<uint16_t*>(out + blk * kBlockBytes)[i] = static_cast<uint16_t>(val);
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(const uint8_t* q, int64_t n_rows, int64_t k, float* out, hipStream_t s) {
+  const int64_t n_groups = n_rows * (k / 4);
+  if (n_groups == 0) return hipSuccess;
+  const int64_t grid = (n_groups + 255) / 256;
+  hipLaunchKernelGGL(dequantize_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, q, n_groups, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* w, const float* imatrix, int64_t n_rows, int64_t k, int encoder,
+                           int rounds, uint8_t* out, hipStream_t s) {
+  const int nb = static_cast<int>(k / kQK);
+  const int64_t n_blocks = n_rows * nb;
+  if (n_blocks == 0) return hipSuccess;
+  const int64_t grid = (n_blocks + 3) / 4;
+  if (encoder == 0)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, w, imatrix,
+                       n_blocks, nb, k, rounds, out);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, w, imatrix,
+                       n_blocks, nb, k, rounds, out);
+  return hipGetLastError();
+}
+
+}  // namespace stq

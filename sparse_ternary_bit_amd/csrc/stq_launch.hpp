@@ -1,0 +1,57 @@
+// Host-side launchers of the libstq kernels (internal to the library).
+// Arguments are validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace stq {
+
+hipError_t launch_dequantize(const uint8_t* q, int64_t n_rows, int64_t k, float* out, hipStream_t s);
+
+hipError_t launch_quantize(const float* w, const float* imatrix, int64_t n_rows, int64_t k, int encoder,
+                           int rounds, uint8_t* out, hipStream_t s);
+
+struct GemvArgs {
+  const uint8_t* w_table;
+  int64_t expert_stride;
+  int64_t n_experts;
+  int64_t n;
+  int64_t k;
+  const void* x;
+  int x_bf16;
+  int64_t x_row_stride;
+  int64_t n_tokens;
+  const int32_t* pair_expert;
+  const int32_t* pair_token;
+  int64_t n_pairs;
+  float* y;
+};
+
+// Scratch needed by launch_gemv for the chosen k split (bytes, 0 if none),
+// and the launch itself.  With splits > 1, `counters` must hold counter_bytes
+// zero bytes (the kernels leave them zero when they finish) and `partial`
+// partial_bytes bytes.
+struct GemvPlan {
+  int splits;          // k split across workgroups
+  int blocks_per_split;
+  int64_t partial_bytes;
+  int64_t counter_bytes;
+};
+GemvPlan plan_gemv(const GemvArgs& a);
+hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& plan, void* counters, void* partial, hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* w_table;
+  int64_t expert_stride;
+  int64_t n_experts;
+  int64_t n;
+  int64_t k;
+  const uint16_t* x;
+  const int32_t* offsets;
+  int64_t total_m;
+  float* y;
+};
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace stq

@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before touching the GPU.  No kernel runs."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_ternary_bit_amd as stq
+    if not os.path.exists(stq.lib_path()):
+        from sparse_ternary_bit_amd import build
+        build.build(verbose=False)
+    return stq.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(stq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for want in ("stq_quantize_rows", "stq_gemv", "stq_grouped_gemm", "stq_dequantize_rows",
+                 "stq_row_bytes", "stq_status_string", "stq_last_error"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_row_bytes(L):
+    assert L.stq_row_bytes(256) == 42
+    assert L.stq_row_bytes(1024) == 168
+    assert L.stq_row_bytes(7168) == 1176
+    for bad in (0, -256, 100, 257):
+        assert L.stq_row_bytes(bad) == -1
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.stq_status_string(s)
+    assert L.stq_status_string(99) == b"unknown status"
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def _err(L):
+    return L.stq_last_error().decode()
+
+
+def test_quantize_rejects_bad_arguments(L):
+    assert L.stq_quantize_rows(FAKE, None, 4, 100, 0, 3, FAKE, None) == 2
+    assert "multiple of 256" in _err(L)
+    assert L.stq_quantize_rows(FAKE, None, 4, 256, 7, 3, FAKE, None) == 1
+    assert L.stq_quantize_rows(FAKE, None, 4, 256, 0, -1, FAKE, None) == 1
+    assert L.stq_quantize_rows(None, None, 4, 256, 0, 3, FAKE, None) == 1
+    assert L.stq_quantize_rows(FAKE + 2, None, 4, 256, 0, 3, FAKE, None) == 3
+    assert L.stq_quantize_rows(FAKE, None, 4, 256, 0, 3, FAKE + 1, None) == 3
+    assert L.stq_quantize_rows(FAKE, None, -1, 256, 0, 3, FAKE, None) == 1
+
+
+def test_dequantize_rejects_bad_arguments(L):
+    assert L.stq_dequantize_rows(FAKE, 2, 300, FAKE, None) == 2
+    assert L.stq_dequantize_rows(FAKE + 1, 2, 256, FAKE, None) == 3
+    assert L.stq_dequantize_rows(FAKE, 2, 256, FAKE + 2, None) == 3
+    assert L.stq_dequantize_rows(None, 2, 256, FAKE, None) == 1
+
+
+def _gemv(L, **kw):
+    a = dict(w=FAKE, stride=4096 * 1176, ne=4, n=4096, k=7168, x=FAKE, xd=1, xs=7168, nt=4,
+             pe=None, pt=None, np_=4, y=FAKE)
+    a.update(kw)
+    return L.stq_gemv(a["w"], a["stride"], a["ne"], a["n"], a["k"], a["x"], a["xd"], a["xs"], a["nt"],
+                      a["pe"], a["pt"], a["np_"], a["y"], None)
+
+
+def test_gemv_rejects_bad_arguments(L):
+    assert _gemv(L, k=1000) == 2
+    assert _gemv(L, ne=0) == 1
+    assert _gemv(L, xd=5) == 1
+    assert _gemv(L, stride=100) == 2
+    assert "expert stride" in _err(L)
+    assert _gemv(L, xs=100) == 2
+    assert _gemv(L, np_=70000) == 2
+    assert _gemv(L, w=FAKE + 8) == 3
+    assert _gemv(L, stride=4096 * 1176 + 8) == 3
+    assert _gemv(L, xs=7169) == 3
+    assert _gemv(L, y=None) == 1
+    assert _gemv(L, np_=-1) == 1
+
+
+def test_gemv_empty_work_is_ok_without_gpu(L):
+    assert _gemv(L, np_=0, w=None, x=None, y=None) == 0
+    assert _gemv(L, n=0, w=None, x=None, y=None) == 0
+
+
+def test_grouped_gemm_rejects_bad_arguments(L):
+    def g(**kw):
+        a = dict(w=FAKE, stride=4096 * 1176, ne=256, n=4096, k=7168, x=FAKE, off=FAKE, m=16, y=FAKE)
+        a.update(kw)
+        return L.stq_grouped_gemm(a["w"], a["stride"], a["ne"], a["n"], a["k"], a["x"], a["off"], a["m"],
+                                  a["y"], None)
+    assert g(k=300) == 2
+    assert g(off=None) == 1
+    assert g(x=FAKE + 8) == 3
+    assert g(ne=70000) == 2
+    assert g(stride=10) == 2
+    assert g(m=-1) == 1
+    assert g(m=0, w=None, x=None, y=None) == 0
