@@ -161,6 +161,51 @@ def row_bytes(k: int) -> int:
     return k // QK * BLOCK_BYTES
 
 
+TILE_ROWS = 64
+
+
+def block_offset(r: int, b: int, n_rows: int, nb: int) -> int:
+    """Byte offset of block b (columns 256b..256b+255) of row r in a packed matrix.
+
+    Reading (the pages fix only the 42-byte block): a matrix of n_rows rows is
+    stored in row tiles of 64 consecutive rows (the last tile holds the
+    n_rows % 64 leftover rows, if any); a tile stores block 0 of each of its
+    rows in row order, then block 1 of each, and so on.
+    """
+    t0 = (r // TILE_ROWS) * TILE_ROWS
+    rows_in_tile = min(TILE_ROWS, n_rows - t0)
+    return (t0 * nb + b * rows_in_tile + (r - t0)) * BLOCK_BYTES
+
+
+def _matrix_offsets(n_rows: int, nb: int) -> np.ndarray:
+    """block_offset for every (row, block), as an array [n_rows, nb]."""
+    r = np.arange(n_rows, dtype=np.int64)[:, None]
+    b = np.arange(nb, dtype=np.int64)[None, :]
+    t0 = (r // TILE_ROWS) * TILE_ROWS
+    rows_in_tile = np.minimum(TILE_ROWS, n_rows - t0)
+    return (t0 * nb + b * rows_in_tile + (r - t0)) * BLOCK_BYTES
+
+
+def pack_matrix(blocks: np.ndarray) -> np.ndarray:
+    """Blocks [n_rows, nb, 42] (row r, block b) -> the packed matrix as flat bytes."""
+    blocks = np.asarray(blocks, dtype=np.uint8)
+    n_rows, nb = blocks.shape[0], blocks.shape[1]
+    out = np.empty(n_rows * nb * BLOCK_BYTES, dtype=np.uint8)
+    off = _matrix_offsets(n_rows, nb)
+    idx = off[..., None] + np.arange(BLOCK_BYTES)
+    out[idx.reshape(-1)] = blocks.reshape(-1)
+    return out
+
+
+def unpack_matrix(q: np.ndarray, n_rows: int, nb: int) -> np.ndarray:
+    """Packed matrix (flat bytes) -> blocks [n_rows, nb, 42]."""
+    q = np.asarray(q, dtype=np.uint8).reshape(-1)
+    if q.shape[0] != n_rows * nb * BLOCK_BYTES:
+        raise ValueError("matrix size does not match n_rows x nb blocks")
+    idx = _matrix_offsets(n_rows, nb)[..., None] + np.arange(BLOCK_BYTES)
+    return q[idx]
+
+
 # -----------------------------------------------------------------------------
 # O3: decode
 # -----------------------------------------------------------------------------
@@ -169,16 +214,16 @@ def fp16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def dequantize_rows(q: np.ndarray, n_rows: int, k: int) -> np.ndarray:
-    """Packed rows [n_rows, k/256*42] -> fp32 weights [n_rows, k].
+    """Packed matrix of n_rows rows (flat, n_rows*k/256*42 bytes) -> fp32 weights [n_rows, k].
 
     Each weight is its block's fp16 scale widened to fp32 times the pattern
     value: +d, -d, or +0.0 in the zero lane ([LEMMY] "Four weights, five
     bits").  The sign is applied by negation, so it is exact for every d.
     """
-    q = np.asarray(q, dtype=np.uint8).reshape(n_rows, -1)
-    if q.shape[1] != row_bytes(k):
-        raise ValueError("row size does not match k")
-    d16, codes = unpack_blocks(q.reshape(-1, BLOCK_BYTES))
+    blocks = unpack_matrix(q, n_rows, k // QK) if k % QK == 0 else None
+    if blocks is None:
+        raise ValueError("k must be a multiple of 256")
+    d16, codes = unpack_blocks(blocks.reshape(-1, BLOCK_BYTES))
     d = fp16_bits_to_f32(d16)[:, None, None]                    # [nb, 1, 1]
     t = CODEBOOK[codes.astype(np.int64)]                         # [nb, 64, 4]
     w = np.where(t > 0, d, np.negative(d))
@@ -292,7 +337,7 @@ def encode_trace(w: np.ndarray, imatrix=None, rounds: int = 3) -> dict:
 
 
 def quantize_rows(w: np.ndarray, imatrix=None, encoder: str = "wls", rounds: int = 3) -> np.ndarray:
-    """Encode fp32 rows [n, k] into packed STQ1_0 rows [n, k/256*42] (uint8).
+    """Encode fp32 rows [n, k] into a packed STQ1_0 matrix (flat uint8, n*k/256*42 bytes).
 
     encoder='wls'  : alternating WLS scale / weighted zero choice (O5), `rounds` rounds.
     encoder='amax' : the original ternary encoder ([ALPHA] bullets: it used
@@ -317,7 +362,7 @@ def quantize_rows(w: np.ndarray, imatrix=None, encoder: str = "wls", rounds: int
         raise ValueError("encoder must be 'wls' or 'amax'")
     codes = codes_from_pattern(z, neg)
     packed = pack_blocks(fp16_scale_bits(d).reshape(-1), codes.reshape(-1, NGROUPS))
-    return packed.reshape(n, nb * BLOCK_BYTES)
+    return pack_matrix(packed.reshape(n, nb, BLOCK_BYTES))
 
 
 # -----------------------------------------------------------------------------
@@ -375,7 +420,8 @@ def grouped_gemm(table: np.ndarray, expert_stride: int, n_rows: int, k: int,
 def tolerance_scale(q: np.ndarray, n_rows: int, k: int, x: np.ndarray) -> np.ndarray:
     """A[t, n] = sum_b d_{n,b} * sum_{k in block b} |x[t, k]| (fp64), the scale
     of the per-element error bound for row n and token t."""
-    d16, _ = unpack_blocks(np.asarray(q, dtype=np.uint8).reshape(-1, BLOCK_BYTES))
+    blocks = unpack_matrix(q, n_rows, k // QK)
+    d16, _ = unpack_blocks(blocks.reshape(-1, BLOCK_BYTES))
     d = np.abs(fp16_bits_to_f32(d16).astype(np.float64)).reshape(n_rows, k // QK)
     ax = np.abs(np.asarray(x, dtype=np.float64).reshape(-1, k // QK, QK)).sum(axis=-1)
     return ax @ d.T

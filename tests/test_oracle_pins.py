@@ -86,6 +86,21 @@ def test_pack_matches_hand_derived_bytes():
         assert raw.tolist() == want.tolist(), ex
 
 
+def test_matrix_layout_matches_hand_derived_offsets():
+    gold = json.load(open(GOLDEN))["matrix_offsets"]
+    n, nb = gold["n_rows"], gold["nb"]
+    for r, b, off in gold["offsets"]:
+        assert O.block_offset(r, b, n, nb) == off, (r, b)
+    # every block has its own 42 bytes and the matrix is exactly n*nb*42 bytes
+    offs = sorted(O.block_offset(r, b, n, nb) for r in range(n) for b in range(nb))
+    assert offs == list(range(0, n * nb * 42, 42))
+    blocks = np.random.default_rng(2).integers(0, 256, size=(n, nb, 42)).astype(np.uint8)
+    flat = O.pack_matrix(blocks)
+    assert np.array_equal(O.unpack_matrix(flat, n, nb), blocks)
+    for r, b, off in gold["offsets"]:
+        assert np.array_equal(flat[off:off + 42], blocks[r, b])
+
+
 def test_every_code_bit_has_its_own_position():
     seen = {}
     for g in range(64):
@@ -143,7 +158,7 @@ def test_quantize_of_decoded_valid_blocks_is_identity(encoder):
     exp = rng.integers(1, 31, size=nb)
     man = rng.integers(0, 1024, size=nb)
     d16 = ((exp << 10) | man).astype(np.uint16)
-    raw = O.pack_blocks(d16, codes).reshape(4, 10 * 42)             # 4 rows x 10 blocks
+    raw = O.pack_matrix(O.pack_blocks(d16, codes).reshape(4, 10, 42))   # 4 rows x 10 blocks
     w = O.dequantize_rows(raw, 4, 2560)
     q = rng.uniform(0.05, 3.0, size=2560).astype(np.float32)
     again = O.quantize_rows(w, q, encoder=encoder, rounds=3)
@@ -462,7 +477,7 @@ def test_gemv_unit_vectors_give_columns_exactly():
 def test_gemv_block_indicator_counts_signs():
     n, k = 6, 768
     q = _small_packed(5, n, k)
-    d16, codes = O.unpack_blocks(q.reshape(-1, 42))
+    d16, codes = O.unpack_blocks(O.unpack_matrix(q, n, 3).reshape(-1, 42))
     d = O.fp16_bits_to_f32(d16).reshape(n, 3)
     codes = codes.reshape(n, 3, 64)
     for b in range(3):
@@ -496,7 +511,7 @@ def test_tolerance_scale_closed_form():
     n, k = 3, 512
     q = _small_packed(10, n, k)
     x = np.ones(k, dtype=np.float32)
-    d16, _ = O.unpack_blocks(q.reshape(-1, 42))
+    d16, _ = O.unpack_blocks(O.unpack_matrix(q, n, 2).reshape(-1, 42))
     d = O.fp16_bits_to_f32(d16).reshape(n, 2).astype(np.float64)
     A = O.tolerance_scale(q, n, k, x)[0]
     assert np.allclose(A, 256.0 * d.sum(axis=1), rtol=0, atol=0)
