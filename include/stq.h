@@ -23,9 +23,15 @@
  *   other lanes in increasing order take -1 when their bit of m is set
  *   (lowest lane -> bit 0), else +1.  Decoded weight = +/-fp32(d), or +0.0
  *   in the zero lane.
- * A packed row of k weights (k a multiple of 256) is k/256 consecutive
- * blocks, block b covering columns 256b..256b+255; a packed matrix is rows
- * back to back, row_bytes = k/256*42 apart.
+ * Matrix layout (also this library's): a matrix of n rows and k columns (k a
+ * multiple of 256) holds n*k/256 blocks, block b of a row covering columns
+ * 256b..256b+255, n*row_bytes(k) bytes in all.  Rows are grouped in tiles of
+ * 64 consecutive rows (the last tile holds the n % 64 leftover rows, if any);
+ * a tile stores block 0 of each of its rows in row order, then block 1 of
+ * each, and so on.  Block b of row r of a matrix starting at byte 0 is at
+ *   (t*nb + b*rows_in_tile + (r - t)) * 42,   t = r - r % 64,
+ *   rows_in_tile = min(64, n - t),            nb = k / 256.
+ * So the 64 rows' block b of a full tile is one contiguous 2688-byte run.
  *
  * Conventions for every entry point:
  *   - array arguments are DEVICE pointers owned by the caller, unless stated;
@@ -82,7 +88,7 @@ int64_t stq_row_bytes(int64_t k);
  *            STQ_ENC_AMAX: d = block max |w|, smallest |w| zeroed; `rounds`
  *              ignored.
  *   rounds   >= 0 (3 is the pages' setting)
- *   out      [n_rows, k/256*42] bytes
+ *   out      packed matrix, n_rows*k/256*42 bytes (layout above)
  * Sums run in fp64 in a fixed order (lanes of a group in order, then a
  * balanced tree of adjacent groups); d is stored as fp16 via fp32
  * (round-to-nearest-even both times, clamped to 65504).  The result is
@@ -91,16 +97,16 @@ int64_t stq_row_bytes(int64_t k);
 stq_status stq_quantize_rows(const float* w, const float* imatrix, int64_t n_rows, int64_t k,
                              int encoder, int rounds, uint8_t* out, stq_stream_t stream);
 
-/* Decode packed rows to fp32: out[r, i] = +/-fp32(d) or +0.0 (bit-exact).
- *   q    [n_rows, k/256*42] bytes, 2-byte aligned
- *   out  [n_rows, k] fp32 */
+/* Decode a packed matrix to fp32: out[r, i] = +/-fp32(d) or +0.0 (bit-exact).
+ *   q    packed matrix of n_rows rows (layout above), 2-byte aligned
+ *   out  [n_rows, k] fp32, row-major */
 stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, float* out,
                                stq_stream_t stream);
 
 /* Gathered decode GEMV over (token, expert) pairs, the STQ1_0 matmul of the
  * decode path (lemmy post 66506, paragraph "Runtime": STQ1_0 kernels run the
  * expert projections).
- *   w_table   expert e's packed [n, k] matrix starts at w_table + e*expert_stride_bytes;
+ *   w_table   expert e's packed n x k matrix starts at w_table + e*expert_stride_bytes;
  *             w_table 16-byte aligned, expert_stride_bytes a multiple of 16 and
  *             >= n*row_bytes(k)
  *   x         activations [n_tokens, k] with row stride x_row_stride elements,

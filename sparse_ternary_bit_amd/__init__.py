@@ -102,22 +102,27 @@ def row_bytes(k: int) -> int:
 
 def quantize_rows(w: torch.Tensor, imatrix: torch.Tensor | None = None, encoder: int = ENC_WLS,
                   rounds: int = 3, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Encode fp32 rows [n, k] on the GPU; returns uint8 [n, k/256*42]."""
+    """Encode fp32 rows [n, k] on the GPU into a packed matrix (flat uint8, n*k/256*42 bytes,
+    64-row tiles, block-major inside a tile)."""
     _on_gpu("w", w, torch.float32)
     n, k = w.shape
     if imatrix is not None:
         _on_gpu("imatrix", imatrix, torch.float32)
     if out is None:
-        out = torch.empty((n, row_bytes(k)), dtype=torch.uint8, device=w.device)
+        out = torch.empty(n * row_bytes(k), dtype=torch.uint8, device=w.device)
     _on_gpu("out", out, torch.uint8)
+    if out.numel() < n * row_bytes(k):
+        raise ValueError("out must hold n*k/256*42 bytes")
     _check("stq_quantize_rows", lib().stq_quantize_rows(w.data_ptr(), _ptr(imatrix), n, k, int(encoder),
                                                         int(rounds), out.data_ptr(), _stream()))
     return out
 
 
 def dequantize_rows(q: torch.Tensor, n: int, k: int, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode packed rows to fp32 [n, k]."""
+    """Decode a packed matrix of n rows to fp32 [n, k]."""
     _on_gpu("q", q, torch.uint8)
+    if q.numel() < n * row_bytes(k):
+        raise ValueError("q must hold n*k/256*42 bytes")
     if out is None:
         out = torch.empty((n, k), dtype=torch.float32, device=q.device)
     _on_gpu("out", out, torch.float32)

@@ -23,13 +23,15 @@ namespace {
 // ---------------------------------------------------------------------------
 // decode: one thread per group of four weights
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ q, int64_t n_groups,
-                                                         float* __restrict__ out) {
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ q, int64_t n_groups, int n,
+                                                         int nb, float* __restrict__ out) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gid >= n_groups) return;
-  const int64_t blk = gid >> 6;
+  const int64_t blk = gid >> 6;  // row-major block index r*nb + b
   const int g = static_cast<int>(gid & 63);
-  const uint8_t* p = q + blk * kBlockBytes;
+  const int r = static_cast<int>(blk / nb);
+  const int b = static_cast<int>(blk - static_cast<int64_t>(r) * nb);
+  const uint8_t* p = q + block_offset(r, b, n, nb);
   const uint32_t d16 = static_cast<uint32_t>(p[0]) | (static_cast<uint32_t>(p[1]) << 8);
   const uint32_t nib = (p[2 + 4 * (g >> 3) + (g & 3)] >> (4 * ((g >> 2) & 1))) & 15u;
   const uint32_t sel = (p[34 + 4 * (g >> 5) + (g & 3)] >> ((g >> 2) & 7)) & 1u;
@@ -89,7 +91,7 @@ __device__ __forceinline__ int choose_zero(const double (&a)[4], const double (&
 
 template <bool kWls>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, const float* __restrict__ imat,
-                                                       int64_t n_blocks, int nb, int64_t k, int rounds,
+                                                       int64_t n_blocks, int n, int nb, int64_t k, int rounds,
                                                        uint8_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -163,7 +165,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   if (i == 0) val = d16;
   else if (i <= 16) val = (vq >> (16 * ((i - 1) & 1))) & 0xFFFFu;
   else val = (vh >> (16 * ((i - 17) & 1))) & 0xFFFFu;
-  if (i < 21) reinterpret_cast<uint16_t*>(out + blk * kBlockBytes)[i] = static_cast<uint16_t>(val);
+  if (i < 21)
+    reinterpret_cast<uint16_t*>(out + block_offset(static_cast<int>(row), b, n, nb))[i] = static_cast<uint16_t>(val);
 }
 
 }  // namespace
@@ -172,7 +175,8 @@ hipError_t launch_dequantize(const uint8_t* q, int64_t n_rows, int64_t k, float*
   const int64_t n_groups = n_rows * (k / 4);
   if (n_groups == 0) return hipSuccess;
   const int64_t grid = (n_groups + 255) / 256;
-  hipLaunchKernelGGL(dequantize_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, q, n_groups, out);
+  hipLaunchKernelGGL(dequantize_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, q, n_groups,
+                     static_cast<int>(n_rows), static_cast<int>(k / kQK), out);
   return hipGetLastError();
 }
 
@@ -184,10 +188,10 @@ hipError_t launch_quantize(const float* w, const float* imatrix, int64_t n_rows,
   const int64_t grid = (n_blocks + 3) / 4;
   if (encoder == 0)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, w, imatrix,
-                       n_blocks, nb, k, rounds, out);
+                       n_blocks, static_cast<int>(n_rows), nb, k, rounds, out);
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, w, imatrix,
-                       n_blocks, nb, k, rounds, out);
+                       n_blocks, static_cast<int>(n_rows), nb, k, rounds, out);
   return hipGetLastError();
 }
 

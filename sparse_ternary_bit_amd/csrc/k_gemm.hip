@@ -72,12 +72,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GArgs a) {
   const int col_in = lane & 15;   // column inside a 16-wide tile (B and D)
   const int quarter = lane >> 4;  // k quarter (A, B) / row quarter (D)
   int ncol[2];
-  const uint8_t* wrow[2];
+  const uint8_t* wrow[2];   // block 0 of this lane's weight row; block b is b * tile_rows * 42 further
+  int64_t bstep[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     ncol[t] = n0 + 32 * wave + 16 * t + col_in;
     const int nc = ncol[t] < a.n ? ncol[t] : a.n - 1;
-    wrow[t] = a.w + static_cast<int64_t>(e) * a.estride + static_cast<int64_t>(nc) * a.nb * kBlockBytes;
+    wrow[t] = a.w + static_cast<int64_t>(e) * a.estride + block_offset(nc, 0, a.n, a.nb);
+    bstep[t] = static_cast<int64_t>(min(kTileRows, a.n - (nc & ~(kTileRows - 1)))) * kBlockBytes;
   }
 
   for (int m0 = row0; m0 < row1; m0 += kMRows) {
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         blk[t] = nxt[t];
-        if (b + 1 < a.nb) nxt[t] = load_block_global(wrow[t] + static_cast<int64_t>(b + 1) * kBlockBytes);
+        if (b + 1 < a.nb) nxt[t] = load_block_global(wrow[t] + static_cast<int64_t>(b + 1) * bstep[t]);
       }
       __syncthreads();  // previous block's reads of s_x are done
       // stage activations rows [m0, m0+128) x k [256b, 256b+256) as bf16, zero past the expert

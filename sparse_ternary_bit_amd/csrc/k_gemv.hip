@@ -4,26 +4,29 @@
 // the speed of IQ1_M (lemmy.durstig.online post 66506, "Runtime"); the design
 // below is this library's, for gfx950.
 //
-// Work unit: a workgroup of 256 threads owns 256 consecutive rows of one
+// Work unit: a workgroup of 512 threads owns 512 consecutive rows of one
 // expert (one row per thread) and a range of 256-weight blocks along k, for
-// up to kMT tokens at a time.  Every (token, expert) pair list is scanned on
-// the device: the first valid pair of an expert leads, and it collects every
-// later pair with that expert, so the expert's weights are streamed once per
-// kMT tokens.
+// up to kMT tokens at a time.  The (token, expert) pair list is scanned on
+// the device: the first valid pair of an expert leads and collects every
+// later pair with that expert, so the expert's weights stream once per kMT
+// tokens.
 //
 // Inner product per block: a group of four weights holds one of 32 patterns,
 // so for each token and group the 32 possible signed sums of its four
-// activations are tabulated in LDS once per workgroup (256 rows share each
-// table).  A row then costs, per group and token, one LDS read addressed by
-// the 5-bit code and one fp32 add; the block's fp16 scale multiplies the
-// block sum.  Threads of a wavefront read the same group's 128-byte table at
-// once, so the reads are bank-conflict free.
+// activations are tabulated in LDS once per workgroup (512 rows share each
+// table).  A row then costs, per group, one bit-field extract of its 5-bit
+// code (already scaled by 4) and, per token, one LDS read with the group's
+// table offset as an immediate plus one fp32 add; the block's fp16 scale
+// multiplies the block sum.  All threads of a wavefront read the same
+// group's 128-byte table at once, so the reads are bank-conflict free.
 //
-// Weights: each wavefront stages its 64 rows x 2 blocks (84 bytes per row)
-// through LDS with coalesced dword loads issued one step ahead; rows are then
-// read back per thread with an odd row pitch (21 dwords), which is
-// conflict free.  Rows whose byte length is not a multiple of 4 use a
-// per-thread direct-load variant.
+// Weights: each wavefront stages its 64 rows x one block (11 dwords per row)
+// through LDS with coalesced dword buffer loads; threads read their row back
+// with an odd pitch (11 dwords), which is conflict free.  Loads for block
+// b+2 are issued while block b is processed (two register sets used in
+// turn), weights first and activations second, the order they are consumed
+// in, so waits never cover younger loads.  Rows whose length in bytes is not
+// a multiple of 4 use a per-thread direct-load variant.
 //
 // k split: when few experts are active, the blocks of a row are split over
 // several workgroups; each writes its partial sums to scratch, and the last
@@ -39,9 +42,11 @@
 namespace stq {
 namespace {
 
-constexpr int kRows = 256;     // rows (= threads) per workgroup
-constexpr int kMT = 4;         // tokens per pass
-constexpr int kStageDw = 21;   // dwords per row per staged step (2 blocks = 84 bytes)
+constexpr int kRows = 512;                 // rows (= threads) per workgroup
+constexpr int kWaves = kRows / 64;
+constexpr int kMT = 4;                     // tokens per pass
+constexpr int kTabBytes = kGroups * 32 * 4;
+constexpr int kTokStride = kTabBytes + 16; // token tables apart by a non-multiple of 256 bytes
 
 struct KArgs {
   const uint8_t* w;
@@ -49,7 +54,6 @@ struct KArgs {
   int n_experts;
   int n;
   int nb;          // blocks per row
-  int row_dw;      // row length in dwords (staged path only)
   const void* x;
   int64_t xstride;
   int n_tokens;
@@ -68,14 +72,14 @@ __device__ __forceinline__ int pair_expert(const KArgs& a, int q) { return a.pe 
 __device__ __forceinline__ int pair_token(const KArgs& a, int q) { return a.pt ? a.pt[q] : q; }
 
 struct Shared {
-  float tab[kMT][kGroups][32];                 // per token: 32 signed sums per group
-  uint32_t stage[4][64 * kStageDw];            // per wavefront: 64 rows x 2 blocks
+  alignas(16) char tab[kMT * kTokStride];   // per token: 32 signed sums per group, 64 groups
+  alignas(16) uint32_t stage[kWaves][kTileRows * kBlockBytes / 4];  // per wavefront: one tile x one block
   int pairs[kMT];
   int toks[kMT];
   int mc;
   int next;
   int flag;
-  unsigned long long ball[4];
+  unsigned long long ball[kWaves];
 };
 
 // Collect up to kMT pairs with expert e and a valid token, from `cursor` on,
@@ -100,7 +104,7 @@ __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
     if (tid == 0) {
       int mc = sh.mc;
       int next = base + kRows;
-      for (int w = 0; w < 4 && mc < kMT; ++w) {
+      for (int w = 0; w < kWaves && mc < kMT; ++w) {
         unsigned long long bm = sh.ball[w];
         while (bm != 0ull && mc < kMT) {
           const int bit = __ffsll(static_cast<long long>(bm)) - 1;
@@ -121,7 +125,7 @@ __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
   }
 }
 
-// Activations of one group (4 values) of token `tok` at column `col`.
+// Activations of one group (4 values) of one token at column `col`.
 template <bool kBf16>
 struct XGroup {
   uint32_t v[kBf16 ? 2 : 4];
@@ -133,18 +137,20 @@ struct XGroup {
     } else {
       const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.x) + tok * a.xstride + col);
 #pragma unroll
-      for (int i = 0; i < (kBf16 ? 2 : 4); ++i) v[i] = p[i];
+      for (int i = 0; i < 4; ++i) v[i] = p[i];
     }
   }
   __device__ __forceinline__ float get(int j) const {
     if constexpr (kBf16) return __uint_as_float(j & 1 ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16));
-    return __uint_as_float(v[j]);
+    else return __uint_as_float(v[j]);
   }
 };
 
 // Table entries 8z..8z+7 of one group for zero lane z.  Entry 8z+m is the sum
 // over the three kept lanes (in order) of -x or +x as bit r of m says.
-__device__ __forceinline__ void build_entries(float x0, float x1, float x2, float x3, int z, float* dst) {
+template <bool kBf16>
+__device__ __forceinline__ void build_entries(const XGroup<kBf16>& xg, int z, char* dst) {
+  const float x0 = xg.get(0), x1 = xg.get(1), x2 = xg.get(2), x3 = xg.get(3);
   const float a = (z == 0) ? x1 : x0;
   const float b = (z <= 1) ? x2 : x1;
   const float c = (z <= 2) ? x3 : x2;
@@ -158,12 +164,11 @@ __device__ __forceinline__ void build_entries(float x0, float x1, float x2, floa
 
 // Sum over the 64 groups of one block of table[code], for MC tokens.
 template <int MC>
-__device__ __forceinline__ void block_dot(const Shared& sh, const Block& blk, float (&acc)[kMT]) {
+__device__ __forceinline__ void block_dot(const char* tab, const Block& blk, float (&acc)[kMT]) {
   const float d = half_bits_to_float(blk.d16);
   float bs[MC];
 #pragma unroll
   for (int m = 0; m < MC; ++m) bs[m] = 0.0f;
-  const char* tab = reinterpret_cast<const char*>(&sh.tab[0][0][0]);
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const uint32_t Q = blk.qs[w];
@@ -173,13 +178,12 @@ __device__ __forceinline__ void block_dot(const Shared& sh, const Block& blk, fl
     const uint32_t cu = ((Q >> 2) & 0x3C3C3C3Cu) | ((Hs >> 1) & 0x40404040u);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t ol = (cl >> (8 * j)) & 0xFFu;
-      const uint32_t ou = (cu >> (8 * j)) & 0xFFu;
+      const uint32_t ol = __builtin_amdgcn_ubfe(cl, 8 * j, 8);
+      const uint32_t ou = __builtin_amdgcn_ubfe(cu, 8 * j, 8);
 #pragma unroll
       for (int m = 0; m < MC; ++m) {
-        const char* tm = tab + m * (kGroups * 32 * 4);
-        bs[m] += *reinterpret_cast<const float*>(tm + (8 * w + j) * 128 + ol);
-        bs[m] += *reinterpret_cast<const float*>(tm + (8 * w + 4 + j) * 128 + ou);
+        bs[m] += *reinterpret_cast<const float*>(tab + ol + (m * kTokStride + (8 * w + j) * 128));
+        bs[m] += *reinterpret_cast<const float*>(tab + ou + (m * kTokStride + (8 * w + 4 + j) * 128));
       }
     }
   }
@@ -187,102 +191,120 @@ __device__ __forceinline__ void block_dot(const Shared& sh, const Block& blk, fl
   for (int m = 0; m < MC; ++m) acc[m] = fmaf(d, bs[m], acc[m]);
 }
 
+// Loads of one block for this thread: its share of the wavefront's tile
+// segment (three 16-byte pieces), or, in a partial tile, the 11 words around
+// its own block; plus the activations of its table items.
+template <bool kBf16>
+struct Pre {
+  uint32_t w[12];
+  XGroup<kBf16> x[2];
+};
+
 // Process blocks [b_begin, b_end) of this workgroup's rows for MC tokens.
-// Rows past n read as zero through the buffer range check and are not stored.
-template <bool kBf16, bool kStaged, int MC>
-__device__ void run_chunk(const KArgs& a, Shared& sh, const uint8_t* wexp, int b_begin, int b_end,
-                          float (&acc)[kMT]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int gi = tid >> 2, zi = tid & 3;  // table item of this thread: group gi, zero lane zi
-  const uint32_t rb = static_cast<uint32_t>(a.nb) * kBlockBytes;
+template <bool kBf16, int MC>
+__device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint8_t* wexp, int b_begin,
+                                          int b_end, float (&acc)[kMT]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // table items of this thread: item i = 256*m + 4*g + z, items tid and tid + 512
+  constexpr int kItems = 256 * MC;
+  const int it_g = (tid >> 2) & 63, it_z = tid & 3;
+  const int m0 = tid >> 8, m1 = m0 + 2;
+  const bool has0 = tid < kItems, has1 = tid + kRows < kItems;
+  int tok[MC];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) tok[m] = __builtin_amdgcn_readfirstlane(sh.toks[m]);
+  int tok0 = 0, tok1 = 0;
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    if (m == m0) tok0 = tok[m];
+    if (m == m1) tok1 = tok[m];
+  }
 
 #pragma unroll
   for (int m = 0; m < kMT; ++m) acc[m] = 0.0f;
+  const char* tab = sh.tab;
 
-  XGroup<kBf16> xg[MC];
-#pragma unroll
-  for (int m = 0; m < MC; ++m) xg[m].load(a, sh.toks[m], static_cast<int64_t>(b_begin) * kQK + 4 * gi);
+  // this wavefront's 64 rows are one tile of the packed matrix
+  const int rowbase = blockIdx.x * kRows + wave * 64;
+  const int valid = max(0, min(kTileRows, a.n - rowbase));
+  const bool full = valid == kTileRows;
+  const uint8_t* tb = wexp + static_cast<int64_t>(min(rowbase, a.n)) * a.nb * kBlockBytes;
+  const uint32_t tile_bytes = static_cast<uint32_t>(valid) * a.nb * kBlockBytes;
+  constexpr uint32_t kSeg = kTileRows * kBlockBytes;   // 2688 bytes = 168 x 16
+  char* st = reinterpret_cast<char*>(&sh.stage[wave][0]);
+  typedef int v4i __attribute__((ext_vector_type(4)));
 
-  if constexpr (kStaged) {
-    // the wavefront's 64 rows x 84 bytes per step; dword it*64+lane of the
-    // step tile is row r = idx/21, word wi = idx%21 (row pitch 21 dwords)
-    const int rowbase = blockIdx.x * kRows + wave * 64;
-    const int valid = max(0, min(64, a.n - rowbase));
-    const uint8_t* wb = wexp + static_cast<int64_t>(rowbase) * rb + static_cast<int64_t>(b_begin) * kBlockBytes;
-    const uint32_t nbytes = static_cast<uint32_t>(valid) * rb;  // rb % 4 == 0 on this path
-    uint32_t voff[kStageDw];
+  auto issue = [&](Pre<kBf16>& p, int b) {
+    if (full) {
+      const Rsrc rs = make_rsrc(tb + static_cast<uint32_t>(b) * kSeg, kSeg);
 #pragma unroll
-    for (int it = 0; it < kStageDw; ++it) {
-      const int idx = it * 64 + lane;
-      const int r = idx / kStageDw;
-      voff[it] = static_cast<uint32_t>(r) * rb + 4u * static_cast<uint32_t>(idx - r * kStageDw);
-    }
-    uint32_t stg[kStageDw];
-    {
-      const Rsrc rs = make_rsrc(wb, nbytes);
+      for (int it = 0; it < 3; ++it) {
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, (it * 64 + lane) * 16, 0, 0);
+        p.w[4 * it] = v.x;
+        p.w[4 * it + 1] = v.y;
+        p.w[4 * it + 2] = v.z;
+        p.w[4 * it + 3] = v.w;
+      }
+    } else {
+      // partial tile: this lane's own block, 11 words from the word holding its first byte
+      const Rsrc rs = make_rsrc(tb, (tile_bytes + 3u) & ~3u);
+      const uint32_t off = (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes;
 #pragma unroll
-      for (int it = 0; it < kStageDw; ++it) stg[it] = buf_u32(rs, voff[it], 0);
+      for (int i = 0; i < 11; ++i) p.w[i] = buf_u32(rs, (off & ~3u) + 4 * i, 0);
+      p.w[11] = off & 2u;
     }
-    uint32_t* st = &sh.stage[wave][0];
+    const int64_t col = static_cast<int64_t>(b) * kQK + 4 * it_g;
+    if (has0) p.x[0].load(a, tok0, col);
+    if (has1) p.x[1].load(a, tok1, col);
+  };
+  auto step = [&](Pre<kBf16>& p, int b) {
+    __syncthreads();  // every wavefront is done with the previous table and stage
+    Block own{};
+    if (full) {
+#pragma unroll
+      for (int it = 0; it < 3; ++it) {
+        if (it < 2 || lane < 40)
+          *reinterpret_cast<uint4*>(st + (it * 64 + lane) * 16) =
+              make_uint4(p.w[4 * it], p.w[4 * it + 1], p.w[4 * it + 2], p.w[4 * it + 3]);
+      }
+    } else {
+      uint32_t v[11];
+#pragma unroll
+      for (int i = 0; i < 11; ++i) v[i] = p.w[i];
+      own = block_from_words(v, p.w[11] != 0);
+    }
+    if (has0) build_entries<kBf16>(p.x[0], it_z, sh.tab + m0 * kTokStride + it_g * 128 + it_z * 32);
+    if (has1) build_entries<kBf16>(p.x[1], it_z, sh.tab + m1 * kTokStride + it_g * 128 + it_z * 32);
+    if (b + 2 < b_end) issue(p, b + 2);
+    __syncthreads();
+    Block blk;
+    if (full) {
+      // row `lane`'s block starts at byte 42*lane of the segment (2-byte aligned; gfx950 reads it unaligned)
+      const char* src = st + kBlockBytes * lane;
+      uint16_t d16;
+      __builtin_memcpy(&d16, __builtin_assume_aligned(src, 2), 2);
+      blk.d16 = d16;
+      __builtin_memcpy(blk.qs, __builtin_assume_aligned(src + 2, 2), 32);
+      __builtin_memcpy(blk.qh, __builtin_assume_aligned(src + 34, 2), 8);
+    } else {
+      blk = own;
+    }
+    block_dot<MC>(tab, blk, acc);
+  };
 
-    for (int b0 = b_begin; b0 < b_end; b0 += 2) {
-      __syncthreads();  // previous step's reads of the table and stage are done
-#pragma unroll
-      for (int it = 0; it < kStageDw; ++it) st[it * 64 + lane] = stg[it];
-      if (b0 + 2 < b_end) {
-        // move the buffer base to the next step; the range check then still
-        // excludes rows past n (every offset of a valid row stays inside)
-        const uint32_t shift = static_cast<uint32_t>(b0 + 2 - b_begin) * kBlockBytes;
-        const Rsrc rs = make_rsrc(wb + shift, nbytes > shift ? nbytes - shift : 0u);
-#pragma unroll
-        for (int it = 0; it < kStageDw; ++it) stg[it] = buf_u32(rs, voff[it], 0);
-      }
-#pragma unroll 1
-      for (int kb = 0; kb < 2; ++kb) {
-        const int b = b0 + kb;
-        if (kb) __syncthreads();
-#pragma unroll
-        for (int m = 0; m < MC; ++m)
-          build_entries(xg[m].get(0), xg[m].get(1), xg[m].get(2), xg[m].get(3), zi, &sh.tab[m][gi][8 * zi]);
-        if (b + 1 < b_end) {
-#pragma unroll
-          for (int m = 0; m < MC; ++m) xg[m].load(a, sh.toks[m], static_cast<int64_t>(b + 1) * kQK + 4 * gi);
-        }
-        __syncthreads();
-        uint32_t v[11];
-        const uint32_t* src = st + lane * kStageDw + (kb ? 10 : 0);
-#pragma unroll
-        for (int i = 0; i < 11; ++i) v[i] = src[i];
-        const Block blk = block_from_words(v, kb != 0);
-        block_dot<MC>(sh, blk, acc);
-      }
-    }
-  } else {
-    const int row = blockIdx.x * kRows + tid;
-    const int64_t valid = max(0, min(kRows, a.n - static_cast<int>(blockIdx.x) * kRows));
-    const uint8_t* wb = wexp + static_cast<int64_t>(blockIdx.x) * kRows * rb;
-    const Rsrc rs = make_rsrc(wb, static_cast<uint32_t>((valid * rb + 3) & ~int64_t(3)));
-    const uint32_t roff = static_cast<uint32_t>(row - static_cast<int>(blockIdx.x) * kRows) * rb;
-    Block nxt = load_block_buf(rs, roff + static_cast<uint32_t>(b_begin) * kBlockBytes);
-    for (int b = b_begin; b < b_end; ++b) {
-      const Block blk = nxt;
-      if (b + 1 < b_end) nxt = load_block_buf(rs, roff + static_cast<uint32_t>(b + 1) * kBlockBytes);
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < MC; ++m)
-        build_entries(xg[m].get(0), xg[m].get(1), xg[m].get(2), xg[m].get(3), zi, &sh.tab[m][gi][8 * zi]);
-      if (b + 1 < b_end) {
-#pragma unroll
-        for (int m = 0; m < MC; ++m) xg[m].load(a, sh.toks[m], static_cast<int64_t>(b + 1) * kQK + 4 * gi);
-      }
-      __syncthreads();
-      block_dot<MC>(sh, blk, acc);
-    }
+  Pre<kBf16> pa, pb;
+  issue(pa, b_begin);
+  if (b_begin + 1 < b_end) issue(pb, b_begin + 1);
+  for (int b = b_begin; b < b_end; b += 2) {
+    step(pa, b);
+    if (b + 1 < b_end) step(pb, b + 1);
   }
 }
 
-template <bool kBf16, bool kStaged>
-__global__ __launch_bounds__(256) void gemv_kernel(KArgs a) {
+template <bool kBf16>
+__global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
   __shared__ Shared sh;
   const int tid = threadIdx.x;
   const int p = blockIdx.z;
@@ -290,8 +312,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(KArgs a) {
   const int row = blockIdx.x * kRows + tid;
   const bool row_ok = row < a.n;
 
-  const int e = pair_expert(a, p);
-  const int tk = pair_token(a, p);
+  // p is uniform, so are its expert and token; say so to keep descriptors in scalar registers
+  const int e = __builtin_amdgcn_readfirstlane(pair_expert(a, p));
+  const int tk = __builtin_amdgcn_readfirstlane(pair_token(a, p));
   if (e < 0 || e >= a.n_experts || tk < 0 || tk >= a.n_tokens) {
     if (split == 0 && row_ok) a.y[static_cast<int64_t>(p) * a.n + row] = __builtin_nanf("");
     return;
@@ -313,15 +336,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(KArgs a) {
   int cursor = p;
   for (;;) {
     gather(a, sh, e, cursor);
-    const int mc = sh.mc;
+    const int mc = __builtin_amdgcn_readfirstlane(sh.mc);
     if (mc == 0) break;
-    cursor = sh.next;
+    cursor = __builtin_amdgcn_readfirstlane(sh.next);
     float acc[kMT];
     switch (mc) {
-      case 1: run_chunk<kBf16, kStaged, 1>(a, sh, wexp, b_begin, b_end, acc); break;
-      case 2: run_chunk<kBf16, kStaged, 2>(a, sh, wexp, b_begin, b_end, acc); break;
-      case 3: run_chunk<kBf16, kStaged, 3>(a, sh, wexp, b_begin, b_end, acc); break;
-      default: run_chunk<kBf16, kStaged, 4>(a, sh, wexp, b_begin, b_end, acc); break;
+      case 1: run_chunk<kBf16, 1>(a, sh, wexp, b_begin, b_end, acc); break;
+      case 2: run_chunk<kBf16, 2>(a, sh, wexp, b_begin, b_end, acc); break;
+      case 3: run_chunk<kBf16, 3>(a, sh, wexp, b_begin, b_end, acc); break;
+      default: run_chunk<kBf16, 4>(a, sh, wexp, b_begin, b_end, acc); break;
     }
     if (row_ok) {
 #pragma unroll
@@ -351,9 +374,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(KArgs a) {
   cursor = p;
   for (;;) {
     gather(a, sh, e, cursor);
-    const int mc = sh.mc;
+    const int mc = __builtin_amdgcn_readfirstlane(sh.mc);
     if (mc == 0) break;
-    cursor = sh.next;
+    cursor = __builtin_amdgcn_readfirstlane(sh.next);
     if (row_ok) {
       for (int m = 0; m < mc; ++m) {
         const int64_t q = sh.pairs[m];
@@ -375,16 +398,12 @@ GemvPlan plan_gemv(const GemvArgs& a) {
   GemvPlan pl{};
   const int nb = static_cast<int>(a.k / kQK);
   const int ntiles = static_cast<int>((a.n + kRows - 1) / kRows);
-  const bool staged = (nb % 2) == 0;
   const int64_t active = std::min<int64_t>(a.n_pairs, a.n_experts);
   const int64_t base_wgs = std::max<int64_t>(1, active * ntiles);
-  int64_t want = (1024 + base_wgs - 1) / base_wgs;  // aim for >= ~1024 workgroups
-  const int step = staged ? 2 : 1;
-  const int max_splits = (nb + step - 1) / step;
-  if (want > max_splits) want = max_splits;
+  int64_t want = (512 + base_wgs - 1) / base_wgs;  // aim for >= ~2 workgroups per CU
+  if (want > nb) want = nb;
   if (want < 1) want = 1;
-  int bps = static_cast<int>((nb + want - 1) / want);
-  bps = (bps + step - 1) / step * step;
+  const int bps = static_cast<int>((nb + want - 1) / want);
   pl.blocks_per_split = bps;
   pl.splits = (nb + bps - 1) / bps;
   if (pl.splits > 1) {
@@ -402,7 +421,6 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* counters, v
   a.n_experts = static_cast<int>(ga.n_experts);
   a.n = static_cast<int>(ga.n);
   a.nb = static_cast<int>(ga.k / kQK);
-  a.row_dw = a.nb * kBlockBytes / 4;
   a.x = ga.x;
   a.xstride = ga.x_row_stride;
   a.n_tokens = static_cast<int>(ga.n_tokens);
@@ -415,15 +433,9 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* counters, v
   a.ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
   a.partial = static_cast<float*>(partial);
   a.counters = static_cast<unsigned*>(counters);
-  const bool staged = (a.nb % 2) == 0;
   const dim3 grid(a.ntiles, pl.splits, a.n_pairs);
-  if (ga.x_bf16) {
-    if (staged) hipLaunchKernelGGL((gemv_kernel<true, true>), grid, dim3(kRows), 0, s, a);
-    else hipLaunchKernelGGL((gemv_kernel<true, false>), grid, dim3(kRows), 0, s, a);
-  } else {
-    if (staged) hipLaunchKernelGGL((gemv_kernel<false, true>), grid, dim3(kRows), 0, s, a);
-    else hipLaunchKernelGGL((gemv_kernel<false, false>), grid, dim3(kRows), 0, s, a);
-  }
+  if (ga.x_bf16) hipLaunchKernelGGL((gemv_kernel<true>), grid, dim3(kRows), 0, s, a);
+  else hipLaunchKernelGGL((gemv_kernel<false>), grid, dim3(kRows), 0, s, a);
   return hipGetLastError();
 }
 

@@ -80,6 +80,7 @@ stq_status stq_quantize_rows(const float* w, const float* imatrix, int64_t n_row
   if (n_rows > 0 && (!w || !out)) return fail(STQ_E_ARG, "stq_quantize_rows: null pointer");
   if (!aligned(w, 4) || !aligned(imatrix, 4)) return fail(STQ_E_ALIGN, "stq_quantize_rows: w/imatrix not 4-byte aligned");
   if (!aligned(out, 2)) return fail(STQ_E_ALIGN, "stq_quantize_rows: out not 2-byte aligned");
+  if (n_rows > INT_MAX || k / STQ_QK > INT_MAX) return fail(STQ_E_SHAPE, "stq_quantize_rows: count exceeds int32");
   if (n_rows * (k / STQ_QK) > (int64_t)INT_MAX * 4) return fail(STQ_E_SHAPE, "stq_quantize_rows: too many blocks");
   hipError_t e = stq::launch_quantize(w, imatrix, n_rows, k, encoder, rounds, out, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "stq_quantize_rows launch");
@@ -91,6 +92,7 @@ stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, floa
   if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "stq_dequantize_rows: k=%lld is not a positive multiple of 256", (long long)k);
   if (n_rows > 0 && (!q || !out)) return fail(STQ_E_ARG, "stq_dequantize_rows: null pointer");
   if (!aligned(q, 2) || !aligned(out, 4)) return fail(STQ_E_ALIGN, "stq_dequantize_rows: q must be 2-byte and out 4-byte aligned");
+  if (n_rows > INT_MAX || k / STQ_QK > INT_MAX) return fail(STQ_E_SHAPE, "stq_dequantize_rows: count exceeds int32");
   if (n_rows * (k / 4) > (int64_t)INT_MAX * 256) return fail(STQ_E_SHAPE, "stq_dequantize_rows: too many groups");
   hipError_t e = stq::launch_dequantize(q, n_rows, k, out, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "stq_dequantize_rows launch");

@@ -23,6 +23,17 @@ namespace stq {
 constexpr int kQK = 256;
 constexpr int kBlockBytes = 42;
 constexpr int kGroups = 64;
+constexpr int kTileRows = 64;
+
+// Packed matrix layout: row tiles of 64 rows (the last tile holds n % 64
+// rows when that is nonzero); inside a tile, block 0 of every row in row
+// order, then block 1, ...  Block b of a full tile's rows is therefore one
+// contiguous, 16-byte aligned run of 64 * 42 = 2688 bytes.
+__device__ __forceinline__ int64_t block_offset(int r, int b, int n, int nb) {
+  const int t0 = r & ~(kTileRows - 1);
+  const int rows = min(kTileRows, n - t0);
+  return (static_cast<int64_t>(t0) * nb + static_cast<int64_t>(b) * rows + (r - t0)) * kBlockBytes;
+}
 
 // One block unpacked into whole words.  Blocks start at even addresses; the
 // two cases below are the two possible alignments modulo 4.  Every load is
@@ -72,8 +83,14 @@ __device__ __forceinline__ Block load_block_global(const uint8_t* p) {
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 
+// Callers pass workgroup-uniform values; readfirstlane states that to the
+// compiler so the descriptor lives in scalar registers (no per-lane loop).
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), kRsrcWord3);
 }
 
 __device__ __forceinline__ uint32_t buf_u32(Rsrc r, uint32_t voff, uint32_t soff) {

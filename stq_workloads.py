@@ -42,7 +42,7 @@ def encode_table(n_experts: int = N_EXPERTS, n: int = N_ROWS, k: int = K, seed: 
     rb = stq.row_bytes(k)
     for e in range(n_experts):
         w = S.torch_expert_weights(seed, e, n, k, device=device)
-        out = table[e * stride: e * stride + n * rb].view(n, rb)
+        out = table[e * stride: e * stride + n * rb]
         stq.quantize_rows(w, imatrix, encoder=encoder, rounds=rounds, out=out)
         del w
     return table, stride

@@ -33,15 +33,20 @@ def table(W):
 
 
 def _packed_rows(t, stride, e, rows):
-    rb = O.row_bytes(K)
-    blob = t[e * stride: e * stride + N * rb].view(N, rb)
-    return blob.index_select(0, torch.as_tensor(rows, device=t.device)).cpu().numpy()
+    """Blocks [len(rows), nb, 42] of rows `rows` of expert e, read from the GPU table."""
+    blob = t[e * stride: e * stride + N * O.row_bytes(K)].cpu().numpy()
+    return O.unpack_matrix(blob, N, K // 256)[np.asarray(rows)]
 
 
 def _oracle_rows(W, e, rows, q):
-    """The oracle's own encoding of rows `rows` of expert e (from the raw fp32 draw)."""
+    """The oracle's own encoding of rows `rows` of expert e (from the raw fp32
+    draw), as a packed matrix of len(rows) rows."""
     w = W.expert_weight_rows(W.TABLE_SEED, e, rows)
     return O.quantize_rows(w, q)
+
+
+def _oracle_blocks(W, e, rows, q):
+    return O.unpack_matrix(_oracle_rows(W, e, rows, q), len(rows), K // 256)
 
 
 def test_table_bytes_match_oracle(W, table):
@@ -49,7 +54,7 @@ def test_table_bytes_match_oracle(W, table):
     rng = np.random.default_rng(0)
     for e in (0, 1, 137, 255):
         rows = np.unique(np.concatenate([[0, 1, 2047, 2048, 4095], rng.integers(0, N, 11)]))
-        assert np.array_equal(_packed_rows(t, stride, e, rows), _oracle_rows(W, e, rows, q)), e
+        assert np.array_equal(_packed_rows(t, stride, e, rows), _oracle_blocks(W, e, rows, q)), e
 
 
 def test_amax_table_bytes_match_oracle(W):
@@ -57,7 +62,8 @@ def test_amax_table_bytes_match_oracle(W):
     t, stride = W.encode_table(n_experts=3, imatrix=q, encoder=1)
     rows = np.array([0, 5, 4095])
     w = W.expert_weight_rows(W.TABLE_SEED, 2, rows)
-    assert np.array_equal(_packed_rows(t, stride, 2, rows), O.quantize_rows(w, None, encoder="amax"))
+    assert np.array_equal(_packed_rows(t, stride, 2, rows),
+                          O.unpack_matrix(O.quantize_rows(w, None, encoder="amax"), len(rows), K // 256))
 
 
 def _check_pairs(W, table, y, pe, pt, xf, pairs, rows):

@@ -44,7 +44,7 @@ def random_blocks(rng, n_rows, nb):
     man = rng.integers(0, 1024, size=n_rows * nb)
     sign = rng.integers(0, 2, size=n_rows * nb)
     d16 = ((sign << 15) | (exp << 10) | man).astype(np.uint16)
-    return O.pack_blocks(d16, codes).reshape(n_rows, nb * 42)
+    return O.pack_matrix(O.pack_blocks(d16, codes).reshape(n_rows, nb, 42))
 
 
 def check_close(y, y_ref, A, tol, what=""):
@@ -57,7 +57,7 @@ def check_close(y, y_ref, A, tol, what=""):
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("n_rows,k", [(1, 256), (3, 768), (37, 1024), (5, 7168)])
+@pytest.mark.parametrize("n_rows,k", [(1, 256), (3, 768), (37, 1024), (5, 7168), (130, 512)])
 def test_dequantize_bit_exact(stq, n_rows, k):
     rng = np.random.default_rng(n_rows * 1000 + k)
     raw = random_blocks(rng, n_rows, k // 256)
