@@ -5,11 +5,11 @@
 // below is this library's, for gfx950.
 //
 // Work unit: a workgroup of 512 threads owns 512 consecutive rows of one
-// expert (one row per thread) and a range of 256-weight blocks along k, for
-// up to kMT tokens at a time.  The (token, expert) pair list is scanned on
-// the device: the first valid pair of an expert leads and collects every
-// later pair with that expert, so the expert's weights stream once per kMT
-// tokens.
+// expert (one row per thread, eight 64-row tiles) and a range of 256-weight
+// blocks along k, for up to kMT tokens at a time.  The (token, expert) pair
+// list is scanned on the device: the first valid pair of an expert leads and
+// collects every later pair with that expert, so the expert's weights stream
+// once per kMT tokens.
 //
 // Inner product per block: a group of four weights holds one of 32 patterns,
 // so for each token and group the 32 possible signed sums of its four
@@ -17,21 +17,22 @@
 // table).  A row then costs, per group, one bit-field extract of its 5-bit
 // code (already scaled by 4) and, per token, one LDS read with the group's
 // table offset as an immediate plus one fp32 add; the block's fp16 scale
-// multiplies the block sum.  All threads of a wavefront read the same
-// group's 128-byte table at once, so the reads are bank-conflict free.
+// multiplies the block sum.  All threads of a wavefront read the same group's
+// 128-byte table at once, so the reads are bank-conflict free.  Tables are
+// double-buffered: while block b is summed from one buffer, block b+1's table
+// is built into the other, one barrier per block.
 //
-// Weights: each wavefront stages its 64 rows x one block (11 dwords per row)
-// through LDS with coalesced dword buffer loads; threads read their row back
-// with an odd pitch (11 dwords), which is conflict free.  Loads for block
-// b+2 are issued while block b is processed (two register sets used in
-// turn), weights first and activations second, the order they are consumed
-// in, so waits never cover younger loads.  Rows whose length in bytes is not
-// a multiple of 4 use a per-thread direct-load variant.
+// Weights: the matrix is stored in 64-row tiles, block-major inside a tile,
+// so a wavefront's 64 rows of block b are one contiguous 2688-byte run.  Each
+// thread loads the 11 aligned words that cover its own 42-byte block with
+// 16 + 16 + 12-byte buffer loads (the wavefront's loads cover the run with no
+// gaps and never leave it) and realigns them with byte permutes.  Loads run
+// two blocks ahead, in the order they are consumed.
 //
-// k split: when few experts are active, the blocks of a row are split over
-// several workgroups; each writes its partial sums to scratch, and the last
-// one to finish (device-scope counter) adds the partials in split order, so
-// the result does not depend on scheduling.
+// k split: when few experts are active the blocks of a row are split over
+// several workgroups; each writes fp32 partial sums to scratch and a second
+// small kernel adds them in split order, so the result does not depend on
+// scheduling.
 #include <math.h>
 
 #include <algorithm>
@@ -47,6 +48,7 @@ constexpr int kWaves = kRows / 64;
 constexpr int kMT = 4;                     // tokens per pass
 constexpr int kTabBytes = kGroups * 32 * 4;
 constexpr int kTokStride = kTabBytes + 16; // token tables apart by a non-multiple of 256 bytes
+constexpr int kBufBytes = kMT * kTokStride;
 
 struct KArgs {
   const uint8_t* w;
@@ -63,17 +65,14 @@ struct KArgs {
   float* y;
   int bps;         // blocks per split
   int splits;
-  int ntiles;
-  float* partial;
-  unsigned* counters;
+  float* partial;  // [splits, n_pairs, n] when splits > 1
 };
 
 __device__ __forceinline__ int pair_expert(const KArgs& a, int q) { return a.pe ? a.pe[q] : 0; }
 __device__ __forceinline__ int pair_token(const KArgs& a, int q) { return a.pt ? a.pt[q] : q; }
 
 struct Shared {
-  alignas(16) char tab[kMT * kTokStride];   // per token: 32 signed sums per group, 64 groups
-  alignas(16) uint32_t stage[kWaves][kTileRows * kBlockBytes / 4];  // per wavefront: one tile x one block
+  alignas(16) char tab[2][kBufBytes];       // two table buffers; per token 32 signed sums x 64 groups
   int pairs[kMT];
   int toks[kMT];
   int mc;
@@ -191,14 +190,26 @@ __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, flo
   for (int m = 0; m < MC; ++m) acc[m] = fmaf(d, bs[m], acc[m]);
 }
 
-// Loads of one block for this thread: its share of the wavefront's tile
-// segment (three 16-byte pieces), or, in a partial tile, the 11 words around
-// its own block; plus the activations of its table items.
-template <bool kBf16>
-struct Pre {
-  uint32_t w[12];
-  XGroup<kBf16> x[2];
+// The 11 aligned words around one thread's block.
+struct Raw {
+  uint32_t w[11];
 };
+
+// Realign with byte permutes: word i of the block body is bytes 2..5 of
+// (w[i+1]:w[i]) when the block starts on a word boundary, and w[i+1] itself
+// when it starts 2 bytes into w[0]; both are one v_perm with a per-thread
+// selector over the same two registers.
+__device__ __forceinline__ Block realign(const Raw& r, bool odd) {
+  const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
+  const uint32_t seld = odd ? 0x0C0C0302u : 0x0C0C0100u;   // selector byte 0x0C gives 0x00
+  Block b;
+  b.d16 = __builtin_amdgcn_perm(r.w[1], r.w[0], seld);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b.qs[i] = __builtin_amdgcn_perm(r.w[i + 1], r.w[i], sel);
+  b.qh[0] = __builtin_amdgcn_perm(r.w[9], r.w[8], sel);
+  b.qh[1] = __builtin_amdgcn_perm(r.w[10], r.w[9], sel);
+  return b;
+}
 
 // Process blocks [b_begin, b_end) of this workgroup's rows for MC tokens.
 template <bool kBf16, int MC>
@@ -221,85 +232,71 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
     if (m == m0) tok0 = tok[m];
     if (m == m1) tok1 = tok[m];
   }
+  const int tab_off0 = m0 * kTokStride + it_g * 128 + it_z * 32;
+  const int tab_off1 = m1 * kTokStride + it_g * 128 + it_z * 32;
 
 #pragma unroll
   for (int m = 0; m < kMT; ++m) acc[m] = 0.0f;
-  const char* tab = sh.tab;
 
-  // this wavefront's 64 rows are one tile of the packed matrix
+  // this wavefront's rows are one tile of the packed matrix
   const int rowbase = blockIdx.x * kRows + wave * 64;
   const int valid = max(0, min(kTileRows, a.n - rowbase));
-  const bool full = valid == kTileRows;
   const uint8_t* tb = wexp + static_cast<int64_t>(min(rowbase, a.n)) * a.nb * kBlockBytes;
-  const uint32_t tile_bytes = static_cast<uint32_t>(valid) * a.nb * kBlockBytes;
-  constexpr uint32_t kSeg = kTileRows * kBlockBytes;   // 2688 bytes = 168 x 16
-  char* st = reinterpret_cast<char*>(&sh.stage[wave][0]);
+  const Rsrc rs = make_rsrc(tb, (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u);
   typedef int v4i __attribute__((ext_vector_type(4)));
+  typedef int v3i __attribute__((ext_vector_type(3)));
 
-  auto issue = [&](Pre<kBf16>& p, int b) {
-    if (full) {
-      const Rsrc rs = make_rsrc(tb + static_cast<uint32_t>(b) * kSeg, kSeg);
-#pragma unroll
-      for (int it = 0; it < 3; ++it) {
-        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, (it * 64 + lane) * 16, 0, 0);
-        p.w[4 * it] = v.x;
-        p.w[4 * it + 1] = v.y;
-        p.w[4 * it + 2] = v.z;
-        p.w[4 * it + 3] = v.w;
-      }
-    } else {
-      // partial tile: this lane's own block, 11 words from the word holding its first byte
-      const Rsrc rs = make_rsrc(tb, (tile_bytes + 3u) & ~3u);
-      const uint32_t off = (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes;
-#pragma unroll
-      for (int i = 0; i < 11; ++i) p.w[i] = buf_u32(rs, (off & ~3u) + 4 * i, 0);
-      p.w[11] = off & 2u;
-    }
+  auto load_w = [&](Raw& r, int b) {
+    const uint32_t off = (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes;
+    const uint32_t o4 = off & ~3u;
+    const v4i p0 = __builtin_amdgcn_raw_buffer_load_b128(rs, o4, 0, 0);
+    const v4i p1 = __builtin_amdgcn_raw_buffer_load_b128(rs, o4 + 16, 0, 0);
+    const v3i p2 = __builtin_amdgcn_raw_buffer_load_b96(rs, o4 + 32, 0, 0);
+    r.w[0] = p0.x; r.w[1] = p0.y; r.w[2] = p0.z; r.w[3] = p0.w;
+    r.w[4] = p1.x; r.w[5] = p1.y; r.w[6] = p1.z; r.w[7] = p1.w;
+    r.w[8] = p2.x; r.w[9] = p2.y; r.w[10] = p2.z;
+  };
+  auto load_x = [&](XGroup<kBf16> (&x)[2], int b) {
     const int64_t col = static_cast<int64_t>(b) * kQK + 4 * it_g;
-    if (has0) p.x[0].load(a, tok0, col);
-    if (has1) p.x[1].load(a, tok1, col);
+    if (has0) x[0].load(a, tok0, col);
+    if (has1) x[1].load(a, tok1, col);
   };
-  auto step = [&](Pre<kBf16>& p, int b) {
-    __syncthreads();  // every wavefront is done with the previous table and stage
-    Block own{};
-    if (full) {
-#pragma unroll
-      for (int it = 0; it < 3; ++it) {
-        if (it < 2 || lane < 40)
-          *reinterpret_cast<uint4*>(st + (it * 64 + lane) * 16) =
-              make_uint4(p.w[4 * it], p.w[4 * it + 1], p.w[4 * it + 2], p.w[4 * it + 3]);
-      }
-    } else {
-      uint32_t v[11];
-#pragma unroll
-      for (int i = 0; i < 11; ++i) v[i] = p.w[i];
-      own = block_from_words(v, p.w[11] != 0);
-    }
-    if (has0) build_entries<kBf16>(p.x[0], it_z, sh.tab + m0 * kTokStride + it_g * 128 + it_z * 32);
-    if (has1) build_entries<kBf16>(p.x[1], it_z, sh.tab + m1 * kTokStride + it_g * 128 + it_z * 32);
-    if (b + 2 < b_end) issue(p, b + 2);
-    __syncthreads();
-    Block blk;
-    if (full) {
-      // row `lane`'s block starts at byte 42*lane of the segment (2-byte aligned; gfx950 reads it unaligned)
-      const char* src = st + kBlockBytes * lane;
-      uint16_t d16;
-      __builtin_memcpy(&d16, __builtin_assume_aligned(src, 2), 2);
-      blk.d16 = d16;
-      __builtin_memcpy(blk.qs, __builtin_assume_aligned(src + 2, 2), 32);
-      __builtin_memcpy(blk.qh, __builtin_assume_aligned(src + 34, 2), 8);
-    } else {
-      blk = own;
-    }
-    block_dot<MC>(tab, blk, acc);
+  auto build = [&](const XGroup<kBf16> (&x)[2], char* t) {
+    if (has0) build_entries<kBf16>(x[0], it_z, t + tab_off0);
+    if (has1) build_entries<kBf16>(x[1], it_z, t + tab_off1);
   };
+  // 42*(b*valid + lane) is 2 mod 4 exactly when b*valid + lane is odd
+  const bool lane_odd = (lane & 1) != 0;
+  char* buf0 = sh.tab[0];
+  char* buf1 = sh.tab[1];
 
-  Pre<kBf16> pa, pb;
-  issue(pa, b_begin);
-  if (b_begin + 1 < b_end) issue(pb, b_begin + 1);
+  // Pipeline over blocks j = b - b_begin: weights of blocks j, j+1 and
+  // activations of blocks j+1, j+2 are in flight; block j uses weight slot
+  // j&1, table buffer j&1, and builds table j+1 from activation slot (j+1)&1.
+  Raw wa, wb;
+  XGroup<kBf16> xa[2], xb[2];
+  auto step = [&](Raw& wcur, XGroup<kBf16> (&xnext)[2], char* tcur, char* tnext, int b) {
+    const bool odd = ((static_cast<uint32_t>(b) * valid) & 1u) ? !lane_odd : lane_odd;
+    const Block blk = realign(wcur, odd);
+    if (b + 1 < b_end) build(xnext, tnext);
+    if (b + 2 < b_end) load_w(wcur, b + 2);
+    if (b + 3 < b_end) load_x(xnext, b + 3);
+    block_dot<MC>(tcur, blk, acc);
+    __syncthreads();  // table b+1 is complete and every thread is done with table b
+  };
+  {
+    load_w(wa, b_begin);
+    if (b_begin + 1 < b_end) load_w(wb, b_begin + 1);
+    XGroup<kBf16> x0[2];
+    load_x(x0, b_begin);
+    if (b_begin + 1 < b_end) load_x(xb, b_begin + 1);
+    if (b_begin + 2 < b_end) load_x(xa, b_begin + 2);
+    build(x0, buf0);
+    __syncthreads();
+  }
   for (int b = b_begin; b < b_end; b += 2) {
-    step(pa, b);
-    if (b + 1 < b_end) step(pb, b + 1);
+    step(wa, xb, buf0, buf1, b);
+    if (b + 1 < b_end) step(wb, xa, buf1, buf0, b + 1);
   }
 }
 
@@ -358,38 +355,22 @@ __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
     }
     __syncthreads();  // sh.pairs is rewritten by the next gather
   }
+}
 
-  if (a.splits == 1) return;
-  // last of the `splits` workgroups of this (expert, row tile) adds the partials in split order
-  __threadfence();
-  __syncthreads();
-  unsigned* ctr = a.counters + static_cast<int64_t>(p) * a.ntiles + blockIdx.x;
-  if (tid == 0) {
-    const unsigned old = atomicAdd(ctr, 1u);
-    sh.flag = (old == static_cast<unsigned>(a.splits - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!sh.flag) return;
-  __threadfence();
-  cursor = p;
-  for (;;) {
-    gather(a, sh, e, cursor);
-    const int mc = __builtin_amdgcn_readfirstlane(sh.mc);
-    if (mc == 0) break;
-    cursor = __builtin_amdgcn_readfirstlane(sh.next);
-    if (row_ok) {
-      for (int m = 0; m < mc; ++m) {
-        const int64_t q = sh.pairs[m];
-        float s = 0.0f;
-        for (int sp = 0; sp < a.splits; ++sp)
-          s += __hip_atomic_load(&a.partial[(static_cast<int64_t>(sp) * a.n_pairs + q) * a.n + row],
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.y[q * a.n + row] = s;
-      }
-    }
-    __syncthreads();
-  }
-  if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// y[p, r] = sum over splits s, in order, of partial[s, p, r], for valid pairs.
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partial, int splits,
+                                                            int64_t plane, const int32_t* __restrict__ pe,
+                                                            const int32_t* __restrict__ pt, int n_experts,
+                                                            int n_tokens, int n, float* __restrict__ y) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= plane) return;
+  const int p = static_cast<int>(i / n);
+  const int e = pe ? pe[p] : 0;
+  const int t = pt ? pt[p] : p;
+  if (e < 0 || e >= n_experts || t < 0 || t >= n_tokens) return;  // the GEMV wrote NaN there
+  float s = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) s += partial[static_cast<int64_t>(sp) * plane + i];
+  y[i] = s;
 }
 
 }  // namespace
@@ -406,14 +387,12 @@ GemvPlan plan_gemv(const GemvArgs& a) {
   const int bps = static_cast<int>((nb + want - 1) / want);
   pl.blocks_per_split = bps;
   pl.splits = (nb + bps - 1) / bps;
-  if (pl.splits > 1) {
-    pl.partial_bytes = static_cast<int64_t>(pl.splits) * a.n_pairs * a.n * 4;
-    pl.counter_bytes = a.n_pairs * ntiles * 4;
-  }
+  if (pl.splits > 1) pl.partial_bytes = static_cast<int64_t>(pl.splits) * a.n_pairs * a.n * 4;
+  pl.counter_bytes = 0;
   return pl;
 }
 
-hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* counters, void* partial, hipStream_t s) {
+hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* /*counters*/, void* partial, hipStream_t s) {
   if (ga.n_pairs == 0 || ga.n == 0) return hipSuccess;
   KArgs a{};
   a.w = ga.w_table;
@@ -430,12 +409,17 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* counters, v
   a.y = ga.y;
   a.bps = pl.blocks_per_split;
   a.splits = pl.splits;
-  a.ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
   a.partial = static_cast<float*>(partial);
-  a.counters = static_cast<unsigned*>(counters);
-  const dim3 grid(a.ntiles, pl.splits, a.n_pairs);
+  const int ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
+  const dim3 grid(ntiles, pl.splits, a.n_pairs);
   if (ga.x_bf16) hipLaunchKernelGGL((gemv_kernel<true>), grid, dim3(kRows), 0, s, a);
   else hipLaunchKernelGGL((gemv_kernel<false>), grid, dim3(kRows), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || pl.splits == 1) return err;
+  const int64_t plane = ga.n_pairs * ga.n;
+  const int64_t grid2 = (plane + 255) / 256;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3(static_cast<unsigned>(grid2)), dim3(256), 0, s, a.partial,
+                     pl.splits, plane, a.pe, a.pt, a.n_experts, a.n_tokens, a.n, a.y);
   return hipGetLastError();
 }
 
