@@ -13,7 +13,14 @@ effective bandwidth over the sweep: algorithmic bytes (each touched expert's
 packed bytes once, plus activations and outputs) divided by GEMV time.
 Kernel durations come from HIP events recorded on the launch stream.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--single-expert]
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--single-expert] [--copy-calibration]
+  python bench.py --counters FETCH_DIR WRITE_DIR   (summarise rocprofv3 counter runs)
+
+HBM traffic: two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+WRITE_SIZE, with --copy-calibration so each run also holds plain copies of a
+known size) are summarised by --counters into profiles/hbm_counters.json,
+keyed by a hash of the kernel sources; `traffic` is reported only while that
+hash matches the current sources.
 """
 from __future__ import annotations
 
@@ -32,6 +39,8 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 BATCHES = (1, 4, 16, 64)
 PREFILL_TOKENS = 2048
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+COPY_MIB = 512               # plain copy used to calibrate the byte counters
+COPY_REPS = 3
 
 
 def kernel_source_hash(name: str) -> str:
@@ -55,6 +64,78 @@ def measured_traffic(kernel_file: str):
     if not ent or ent.get("source_hash") != kernel_source_hash(kernel_file):
         return None
     return ent.get("bytes_per_launch")
+
+
+def _read_counter_csvs(root: str, counter: str):
+    """[(kernel_name, value)] per dispatch from rocprofv3 counter_collection.csv files."""
+    import csv
+    import glob
+    per = {}
+    for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (f, r.get("Dispatch_Id"))
+                name = r.get("Kernel_Name", "")
+                per[key] = (name, per.get(key, (name, 0.0))[1] + float(r["Counter_Value"]))
+    return list(per.values())
+
+
+def summarise_counters(fetch_dir: str, write_dir: str) -> int:
+    """Per-call HBM bytes of the GEMV (gemv_kernel plus its split reduction)
+    and of the grouped GEMM, from FETCH_SIZE and WRITE_SIZE runs (KiB per
+    dispatch), each scaled by the factor that makes the plain copies in the
+    same run read and write exactly their size."""
+    out = {}
+    lines = []
+    factors = {}
+    sums = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _read_counter_csvs(d, counter)
+        copies = [v for (n, v) in rows if "copyBuffer" in n or "copy_kernel" in n]
+        if not copies:
+            print(f"no copy kernel dispatches in {d}", file=sys.stderr)
+            return 1
+        copy_kib = COPY_MIB * 1024.0
+        big = [v for v in copies if v > 0.25 * copy_kib]
+        f = copy_kib / (sum(big) / len(big))
+        factors[counter] = f
+        sums[counter] = {
+            "gemv": (sum(v for (n, v) in rows if "gemv_kernel" in n), sum(1 for (n, _) in rows if "gemv_kernel" in n)),
+            "reduce": (sum(v for (n, v) in rows if "reduce_splits_kernel" in n),
+                       sum(1 for (n, _) in rows if "reduce_splits_kernel" in n)),
+            "gemm": (sum(v for (n, v) in rows if "grouped_gemm_kernel" in n),
+                     sum(1 for (n, _) in rows if "grouped_gemm_kernel" in n)),
+        }
+        lines.append(f"{counter}: plain copy of {COPY_MIB} MiB read as {sum(big) / len(big):.0f} KiB "
+                     f"(mean of {len(big)}), scale factor {f:.4f}")
+    calls = sums["FETCH_SIZE"]["gemv"][1]
+    if calls == 0 or calls != sums["WRITE_SIZE"]["gemv"][1]:
+        print("GEMV dispatch counts differ between the runs", file=sys.stderr)
+        return 1
+    gemv_fetch = (sums["FETCH_SIZE"]["gemv"][0] + sums["FETCH_SIZE"]["reduce"][0]) * 1024 * factors["FETCH_SIZE"] / calls
+    gemv_write = (sums["WRITE_SIZE"]["gemv"][0] + sums["WRITE_SIZE"]["reduce"][0]) * 1024 * factors["WRITE_SIZE"] / calls
+    out["k_gemv.hip"] = {"source_hash": kernel_source_hash("k_gemv.hip"), "calls": calls,
+                         "fetch_bytes_per_call": round(gemv_fetch), "write_bytes_per_call": round(gemv_write),
+                         "bytes_per_launch": round(gemv_fetch + gemv_write),
+                         "scale_factors": {k: round(v, 5) for k, v in factors.items()}}
+    lines.append(f"stq_gemv (gemv_kernel + reduce_splits_kernel), {calls} calls: "
+                 f"fetch {gemv_fetch / 1e6:.2f} MB, write {gemv_write / 1e6:.2f} MB per call")
+    g = sums["FETCH_SIZE"]["gemm"][1]
+    if g and g == sums["WRITE_SIZE"]["gemm"][1]:
+        gf = sums["FETCH_SIZE"]["gemm"][0] * 1024 * factors["FETCH_SIZE"] / g
+        gw = sums["WRITE_SIZE"]["gemm"][0] * 1024 * factors["WRITE_SIZE"] / g
+        out["k_gemm.hip"] = {"source_hash": kernel_source_hash("k_gemm.hip"), "calls": g,
+                             "fetch_bytes_per_call": round(gf), "write_bytes_per_call": round(gw),
+                             "bytes_per_launch": round(gf + gw),
+                             "scale_factors": {k: round(v, 5) for k, v in factors.items()}}
+        lines.append(f"grouped_gemm_kernel, {g} calls: fetch {gf / 1e6:.2f} MB, write {gw / 1e6:.2f} MB per call")
+    with open(PROFILE_COUNTERS, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print("\n".join(lines))
+    return 0
 
 
 def cpu_baseline(seconds: float):
@@ -96,7 +177,13 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--single-expert", action="store_true",
                     help="also time the batch-1 single-expert GEMV over 100 resident experts")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"after timing, copy {COPY_MIB} MiB device to device {COPY_REPS} times (counter calibration)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/hbm_counters.json")
     args = ap.parse_args()
+    if args.counters:
+        return summarise_counters(*args.counters)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the STQ1_0 path here has no multi-GPU mode "
@@ -187,6 +274,14 @@ def main() -> int:
         run_step(s, rec)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_MIB << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_REPS):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------- results ----------------
     gemv_ms = [a.elapsed_time(b) for (_, _, _, _, a, b) in rec["gemv"]]
