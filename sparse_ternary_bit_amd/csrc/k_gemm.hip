@@ -1,22 +1,40 @@
-// Grouped STQ1_0 GEMM for the prefill path: for each expert e,
-// Y[rows of e] = X[rows of e] * W_e^T, rows grouped by expert.
+// Grouped GEMM of the prefill path: for every expert e, the tokens routed to
+// it (rows offsets[e] .. offsets[e+1]-1 of x_sorted, bf16) times the expert's
+// STQ1_0 matrix, y[r, :] = W_e x_sorted[r, :], fp32 out.
 //
-// The pages give the format and say STQ1_0 has GPU kernels (lemmy.durstig.online
-// post 66506, "Runtime"); this is a dense contraction once the ternary
-// patterns are expanded, so it runs on gfx950 matrix cores:
-// v_mfma_f32_16x16x32_bf16, bf16 activations times exactly representable
-// {-1, 0, +1} weights, fp32 accumulation.  The fp16 block scale d of each
-// 256-weight block multiplies the block's partial product in fp32 (one FMA per
-// output per block), so the products stay exact.
+// The pages say only that STQ1_0 runs through dedicated GPU kernels
+// (lemmy.durstig.online post 66506, "Runtime"); a prefill batch makes this a
+// real dense contraction, so it runs on the bf16 matrix cores of gfx950
+// (v_mfma_f32_16x16x32_bf16).  Ternary weights are exact in bf16 and a bf16 x
+// bf16 product is exact in fp32; sums are fp32, and each 256-weight block's
+// partial sum is scaled by its fp32(d) once (one FMA per output per block).
 //
-// Tiling: a workgroup (4 wavefronts) owns 128 output columns of one expert
-// and up to 128 of its rows at a time; each wavefront owns 32 columns (two
-// 16-column MFMA tiles) and every 16-row tile of the rows.  Per 256-weight
-// block, the workgroup stages the activation tile (rows x 256 bf16) in LDS;
-// each lane expands its own weights straight from the packed block: in MFMA
-// step s (32 k values) lane quarter j takes groups 8s+j and 8s+4+j, i.e. the
-// two nibbles of byte j of code word s, and the activation fragment is read
-// with the same k order, so A and B agree on every k.
+// Work unit: a workgroup of 8 wavefronts owns 512 weight rows (one 64-row
+// tile of the packed matrix per wavefront) of one expert and all of that
+// expert's tokens, in passes of at most 80 tokens (5 tiles of 16).  Every
+// weight is therefore decoded once per pass, and each decoded MFMA operand
+// is reused for every token tile of the pass.
+//
+// Per 256-weight block b:
+//   * activations of block b+1 for the pass stream from global memory
+//     straight into LDS (16-byte direct loads) into the second of two
+//     buffers; a token's 32 16-byte chunks are stored XOR-swizzled by the
+//     token index so the matrix-operand reads below are bank-conflict free;
+//   * each wavefront's contiguous tile run of block b+1 streams into LDS the
+//     same way; each lane then reads its own row's 42-byte block there,
+//     realigns it and turns it into four 16-byte records, one per MFMA
+//     k-quarter: for each of
+//     the block's 8 k-steps the quarter's two group codes, pre-scaled by 4 so
+//     a code is directly a byte offset into the pattern table;
+//   * per pair of k-steps the MFMA lanes read one record word; per k-step a
+//     lane extracts two codes (two bit-field extracts) and reads the bf16 lanes of
+//     both patterns from a 32-entry table in LDS (two 8-byte reads): that is
+//     the whole weight decode;
+//   * after the block's 8 k-steps the fp32 partial sums are scaled by the
+//     rows' d into the fp32 totals.
+// One barrier per block.  Workgroups of one expert are launched on the same
+// XCD (workgroup ids are dealt to the 8 XCDs round robin), so the expert's
+// activations are fetched once into that XCD's L2 and shared by its 8 slabs.
 #include "stq_device.hpp"
 #include "stq_launch.hpp"
 
@@ -27,148 +45,262 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kCols = 128;    // output columns per workgroup
-constexpr int kMRows = 128;   // rows per pass
-constexpr int kMSub = kMRows / 16;
-constexpr int kPitch = 264;   // LDS row pitch of the activation tile, bf16 elements
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kSlab = kWaves * kTileRows;   // 512 weight rows per workgroup
+constexpr int kMaxTiles = 5;                // token tiles of 16 per pass
+constexpr int kMaxTok = kMaxTiles * 16;     // 80 tokens per pass
+constexpr int kRowBytes = kQK * 2;          // one token's 256 activations
+constexpr int kXBuf = kMaxTok * kRowBytes;  // 40960 bytes per buffer
+constexpr int kXcds = 8;
+constexpr int kWRaw = 3 * 1024;             // 16-byte aligned window over one 2688-byte tile run
 
 struct GArgs {
   const uint8_t* w;
   int64_t estride;
+  int n_experts;
   int n;
   int nb;
-  const uint16_t* x;
   int64_t k;
+  const uint16_t* x;
   const int32_t* offsets;
-  int total_m;
   float* y;
+  int nslab;
+  int vec4;  // n % 4 == 0: outputs stored 16 bytes at a time
 };
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+struct Smem {
+  // Pattern table: entry c of lut[0..31] holds lanes 0,1 of code c as bf16,
+  // entry c of lut[32..63] lanes 2,3.  Kept at byte 0 so a code times 4 is
+  // its address.
+  uint32_t lut[64];
+  float dsc[kWaves][kTileRows];           // fp32(d) of each row's current block
+  u32x4_t rec[kWaves][4][4][16];          // [wave][row tile][k quarter][row]
+  alignas(16) char x[2][kXBuf];           // activations, current and next block
+  alignas(16) char wraw[kWaves][kWRaw];   // each wavefront's tile run of the next block
+};
 
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GArgs a) {
-  __shared__ uint16_t s_x[kMRows * kPitch];
-  __shared__ uint2 s_lut[32];
+// A zero the compiler cannot see through: the first MFMA of each block adds
+// to these registers instead of to freshly zeroed accumulators.
+__device__ __forceinline__ float opaque_zero() {
+  float z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int e = blockIdx.y;
-  const int n0 = blockIdx.x * kCols;
-  // rows of expert e, clamped to [0, total_m] so bad offsets cannot reach outside x or y
-  const int row0 = max(0, min(a.offsets[e], a.total_m));
-  const int row1 = max(row0, min(a.offsets[e + 1], a.total_m));
-  if (row1 <= row0) return;
+// A pass: tokens [row0, row0 + mt) of the sorted activations, NT = ceil(mt/16).
+template <int NT>
+__device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t* wexp, int slab, int64_t row0,
+                                         int mt) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r = lane & 15;
 
-  // pattern table: code -> four bf16 of {-1, 0, +1}
-  if (tid < 32) {
-    uint32_t h[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = code_lane_value(static_cast<uint32_t>(tid), j);
-      h[j] = t == 0 ? 0u : (t > 0 ? 0x3F80u : 0xBF80u);
+  // this wavefront's weight rows: one 64-row tile of the packed matrix
+  const int trow0 = slab * kSlab + wave * kTileRows;
+  const int valid = max(0, min(kTileRows, a.n - trow0));
+  const uint8_t* tb = wexp + static_cast<int64_t>(min(trow0, a.n)) * a.nb * kBlockBytes;
+  const Rsrc rs = make_rsrc(tb, (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u);
+
+  // activations: 2 tokens (64 chunks of 16 bytes) per wavefront instruction
+  const int n_ins = (mt + 1) >> 1;
+  const int st_t = lane >> 5, st_p = lane & 31;
+  auto stage_x = [&](int b, int buf) {
+    for (int j = wave; j < n_ins; j += kWaves) {
+      const int t = 2 * j + st_t;
+      const int c = st_p ^ (t & 7);
+      const int tt = min(t, mt - 1);
+      const uint16_t* g = a.x + (row0 + tt) * a.k + static_cast<int64_t>(b) * kQK + 8 * c;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g),
+                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                           reinterpret_cast<uintptr_t>(sh.x[buf] + j * 1024)),
+                                       16, 0, 0);
     }
-    s_lut[tid] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  };
+
+  // the tile run of block b (valid * 42 bytes) into this wavefront's window,
+  // from the 16-byte boundary at or below its start; the buffer range check
+  // turns bytes past the tile into zeros
+  auto run_start = [&](int b) { return static_cast<uint32_t>(b) * valid * kBlockBytes; };
+  auto stage_w = [&](int b) {
+    const uint32_t st = run_start(b) & ~15u;
+#pragma unroll
+    for (int j = 0; j < kWRaw / 1024; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(sh.wraw[wave] + j * 1024)),
+          16, static_cast<int>(st + j * 1024 + lane * 16), 0, 0, 0);
+  };
+  // this lane's block out of the window: the 11 aligned words around it
+  auto block_from_window = [&](int b) {
+    const uint32_t off = (run_start(b) & 15u) + lane * kBlockBytes;
+    const uint32_t* wv = reinterpret_cast<const uint32_t*>(sh.wraw[wave] + (off & ~3u));
+    RawBlock rw;
+#pragma unroll
+    for (int i = 0; i < 11; ++i) rw.w[i] = wv[i];
+    return realign_block(rw, (off & 2u) != 0);
+  };
+
+  // records of one block from this lane's own row
+  auto make_records = [&](const Block& blk) {
+    uint32_t cl[8], cu[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t W = blk.qs[s];
+      const uint32_t QH = blk.qh[s >> 2];
+      const int sh6 = 6 - 2 * (s & 3);
+      // byte j of cl: 4 * code of group 8s+j; of cu: 4 * code of group 8s+4+j
+      cl[s] = ((W << 2) & 0x3C3C3C3Cu) | ((QH << sh6) & 0x40404040u);
+      cu[s] = ((W >> 2) & 0x3C3C3C3Cu) | (((QH >> 1) << sh6) & 0x40404040u);
+    }
+    // quarter q covers groups 8s+2q, 8s+2q+1 of k-step s: bytes (2q, 2q+1) of
+    // cl for q < 2, of cu for q >= 2
+    u32x4_t rq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rq[0][i] = __builtin_amdgcn_perm(cl[2 * i + 1], cl[2 * i], 0x05040100u);
+      rq[1][i] = __builtin_amdgcn_perm(cl[2 * i + 1], cl[2 * i], 0x07060302u);
+      rq[2][i] = __builtin_amdgcn_perm(cu[2 * i + 1], cu[2 * i], 0x05040100u);
+      rq[3][i] = __builtin_amdgcn_perm(cu[2 * i + 1], cu[2 * i], 0x07060302u);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) sh.rec[wave][lane >> 4][qq][lane & 15] = rq[qq];
+    sh.dsc[wave][lane] = half_bits_to_float(blk.d16);
+  };
+
+
+  // B operand addresses: token 16*bt + r, chunk (4s + q) ^ (r & 7)
+  const int u = q ^ (r & 7);
+  const int xb_even = r * kRowBytes + u * 16;
+  const int xb_odd = r * kRowBytes + (u ^ 4) * 16;
+
+  const f32x4_t zero4 = {opaque_zero(), opaque_zero(), opaque_zero(), opaque_zero()};
+  f32x4_t tot[4][NT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tot[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: block 0
+  stage_x(0, 0);
+  stage_w(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads have landed
+  make_records(block_from_window(0));
+  __syncthreads();
+
+  for (int b = 0; b < a.nb; ++b) {
+    const int buf = b & 1;
+    const bool more = b + 1 < a.nb;
+    if (more) {
+      stage_x(b + 1, buf ^ 1);
+      stage_w(b + 1);
+    }
+    const char* xs = sh.x[buf];
+    const char* lut = reinterpret_cast<const char*>(sh.lut);
+
+    f32x4_t part[4][NT];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8_t A[4];
+      uint32_t Rw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Rw[i] = sh.rec[wave][i][q][r][s >> 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = Rw[i];
+        const uint32_t c1 = __builtin_amdgcn_ubfe(w, 16 * (s & 1), 8);
+        const uint32_t c2 = __builtin_amdgcn_ubfe(w, 16 * (s & 1) + 8, 8);
+        u32x4_t v;
+        v[0] = *reinterpret_cast<const uint32_t*>(lut + c1);
+        v[1] = *reinterpret_cast<const uint32_t*>(lut + c1 + 128);
+        v[2] = *reinterpret_cast<const uint32_t*>(lut + c2);
+        v[3] = *reinterpret_cast<const uint32_t*>(lut + c2 + 128);
+        A[i] = __builtin_bit_cast(bf16x8_t, v);
+      }
+      const int xo = ((s & 1) ? xb_odd + 64 * (s - 1) : xb_even + 64 * s);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(xs + xo + t * 16 * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t c = (s == 0) ? zero4 : part[i][t];
+          part[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], B, c, 0, 0, 0);
+        }
+      }
+    }
+    // scale the block's partial sums: rows 16i + 4q + j of the tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sh.dsc[wave][16 * i + 4 * q]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tot[i][t][j] = fmaf(d4[j], part[i][t][j], tot[i][t][j]);
+    }
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // block b+1's weights and activations are in LDS
+      make_records(block_from_window(b + 1));
+    }
+    __syncthreads();
   }
 
-  const int col_in = lane & 15;   // column inside a 16-wide tile (B and D)
-  const int quarter = lane >> 4;  // k quarter (A, B) / row quarter (D)
-  int ncol[2];
-  const uint8_t* wrow[2];   // block 0 of this lane's weight row; block b is b * tile_rows * 42 further
-  int64_t bstep[2];
+  // y[row0 + 16t + r, trow0 + 16i + 4q + j]
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    ncol[t] = n0 + 32 * wave + 16 * t + col_in;
-    const int nc = ncol[t] < a.n ? ncol[t] : a.n - 1;
-    wrow[t] = a.w + static_cast<int64_t>(e) * a.estride + block_offset(nc, 0, a.n, a.nb);
-    bstep[t] = static_cast<int64_t>(min(kTileRows, a.n - (nc & ~(kTileRows - 1)))) * kBlockBytes;
-  }
-
-  for (int m0 = row0; m0 < row1; m0 += kMRows) {
-    const int mrows = min(kMRows, row1 - m0);
-    const int nms = (mrows + 15) >> 4;
-    f32x4_t acc[kMSub][2];
+  for (int t = 0; t < NT; ++t) {
+    const int tok = 16 * t + r;
+    if (tok >= mt) continue;
+    float* yr = a.y + (row0 + tok) * a.n;
 #pragma unroll
-    for (int ms = 0; ms < kMSub; ++ms)
+    for (int i = 0; i < 4; ++i) {
+      const int col = trow0 + 16 * i + 4 * q;
+      if (a.vec4 && col + 3 < a.n) {
+        *reinterpret_cast<f32x4_t*>(yr + col) = tot[i][t];
+      } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) acc[ms][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    Block nxt[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) nxt[t] = load_block_global(wrow[t]);
-
-    for (int b = 0; b < a.nb; ++b) {
-      Block blk[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        blk[t] = nxt[t];
-        if (b + 1 < a.nb) nxt[t] = load_block_global(wrow[t] + static_cast<int64_t>(b + 1) * bstep[t]);
-      }
-      __syncthreads();  // previous block's reads of s_x are done
-      // stage activations rows [m0, m0+128) x k [256b, 256b+256) as bf16, zero past the expert
-#pragma unroll
-      for (int u = 0; u < (kMRows * 32) / 256; ++u) {
-        const int c = tid + 256 * u;
-        const int r = c >> 5, c16 = c & 31;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < mrows)
-          v = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(m0 + r) * a.k + 256 * b + 8 * c16);
-        *reinterpret_cast<uint4*>(&s_x[r * kPitch + 8 * c16]) = v;
-      }
-      __syncthreads();
-
-      f32x4_t part[kMSub][2];
-#pragma unroll
-      for (int ms = 0; ms < kMSub; ++ms)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) part[ms][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        bf16x8_t bfrag[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint32_t Q = blk[t].qs[s];
-          const uint32_t H = blk[t].qh[s >> 2] >> (8 * quarter + 2 * (s & 3));
-          const uint32_t c1 = ((Q >> (8 * quarter)) & 15u) | ((H & 1u) << 4);
-          const uint32_t c2 = ((Q >> (8 * quarter + 4)) & 15u) | ((H & 2u) << 3);
-          const uint2 p1 = s_lut[c1];
-          const uint2 p2 = s_lut[c2];
-          bfrag[t] = as_bf16x8(u32x4_t{p1.x, p1.y, p2.x, p2.y});
-        }
-#pragma unroll
-        for (int ms = 0; ms < kMSub; ++ms) {
-          if (ms < nms) {
-            const uint16_t* ap = &s_x[(16 * ms + col_in) * kPitch + 32 * s + 4 * quarter];
-            const uint2 a1 = *reinterpret_cast<const uint2*>(ap);
-            const uint2 a2 = *reinterpret_cast<const uint2*>(ap + 16);
-            const bf16x8_t afrag = as_bf16x8(u32x4_t{a1.x, a1.y, a2.x, a2.y});
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-              part[ms][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[t], part[ms][t], 0, 0, 0);
-          }
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float d = half_bits_to_float(blk[t].d16);
-#pragma unroll
-        for (int ms = 0; ms < kMSub; ++ms)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ms][t][r] = fmaf(d, part[ms][t][r], acc[ms][t][r]);
+        for (int j = 0; j < 4; ++j)
+          if (col + j < a.n) yr[col + j] = tot[i][t][j];
       }
     }
+  }
+}
 
-    // D layout: lane holds rows 4*quarter + r of the 16-row tile, column col_in
-#pragma unroll
-    for (int ms = 0; ms < kMSub; ++ms) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (ncol[t] >= a.n) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rr = 16 * ms + 4 * quarter + r;
-          if (rr < mrows) a.y[static_cast<int64_t>(m0 + rr) * a.n + ncol[t]] = acc[ms][t][r];
-        }
-      }
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GArgs a) {
+  __shared__ Smem sh;
+  // workgroup -> (expert, slab): the slabs of one expert share an XCD
+  const int wg = blockIdx.x;
+  const int xcd = wg % kXcds;
+  const int local = wg / kXcds;
+  const int slab = local % a.nslab;
+  const int e = (local / a.nslab) * kXcds + xcd;
+  if (e >= a.n_experts) return;
+  const int m0 = a.offsets[e];
+  const int m = a.offsets[e + 1] - m0;
+  if (m <= 0) return;
+
+  if (threadIdx.x < 32) {
+    const uint32_t c = threadIdx.x;
+    auto bf = [&](int lane) -> uint32_t {
+      const int t = code_lane_value(c, lane);
+      return t == 0 ? 0u : (t > 0 ? 0x3F80u : 0xBF80u);  // bf16 +1, -1
+    };
+    sh.lut[c] = bf(0) | (bf(1) << 16);
+    sh.lut[32 + c] = bf(2) | (bf(3) << 16);
+  }
+  __syncthreads();
+
+  const uint8_t* wexp = a.w + static_cast<int64_t>(e) * a.estride;
+  const int np = (m + kMaxTok - 1) / kMaxTok;
+  const int per = (m + np - 1) / np;
+  for (int p = 0; p < np; ++p) {
+    const int base = p * per;
+    const int mt = min(per, m - base);
+    const int64_t row0 = static_cast<int64_t>(m0) + base;
+    switch ((mt + 15) >> 4) {
+      case 1: run_pass<1>(a, sh, wexp, slab, row0, mt); break;
+      case 2: run_pass<2>(a, sh, wexp, slab, row0, mt); break;
+      case 3: run_pass<3>(a, sh, wexp, slab, row0, mt); break;
+      case 4: run_pass<4>(a, sh, wexp, slab, row0, mt); break;
+      default: run_pass<5>(a, sh, wexp, slab, row0, mt); break;
     }
   }
 }
@@ -180,15 +312,18 @@ hipError_t launch_grouped_gemm(const GemmArgs& ga, hipStream_t s) {
   GArgs a{};
   a.w = ga.w_table;
   a.estride = ga.expert_stride;
+  a.n_experts = static_cast<int>(ga.n_experts);
   a.n = static_cast<int>(ga.n);
   a.nb = static_cast<int>(ga.k / kQK);
-  a.x = ga.x;
   a.k = ga.k;
+  a.x = ga.x;
   a.offsets = ga.offsets;
-  a.total_m = static_cast<int>(ga.total_m);
   a.y = ga.y;
-  const dim3 grid(static_cast<unsigned>((ga.n + kCols - 1) / kCols), static_cast<unsigned>(ga.n_experts));
-  hipLaunchKernelGGL(grouped_gemm_kernel, grid, dim3(256), 0, s, a);
+  a.nslab = static_cast<int>((ga.n + kSlab - 1) / kSlab);
+  a.vec4 = (ga.n % 4) == 0;
+  const int64_t groups = (ga.n_experts + kXcds - 1) / kXcds;
+  const int64_t grid = groups * kXcds * a.nslab;
+  hipLaunchKernelGGL(grouped_gemm_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -190,27 +190,6 @@ __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, flo
   for (int m = 0; m < MC; ++m) acc[m] = fmaf(d, bs[m], acc[m]);
 }
 
-// The 11 aligned words around one thread's block.
-struct Raw {
-  uint32_t w[11];
-};
-
-// Realign with byte permutes: word i of the block body is bytes 2..5 of
-// (w[i+1]:w[i]) when the block starts on a word boundary, and w[i+1] itself
-// when it starts 2 bytes into w[0]; both are one v_perm with a per-thread
-// selector over the same two registers.
-__device__ __forceinline__ Block realign(const Raw& r, bool odd) {
-  const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
-  const uint32_t seld = odd ? 0x0C0C0302u : 0x0C0C0100u;   // selector byte 0x0C gives 0x00
-  Block b;
-  b.d16 = __builtin_amdgcn_perm(r.w[1], r.w[0], seld);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) b.qs[i] = __builtin_amdgcn_perm(r.w[i + 1], r.w[i], sel);
-  b.qh[0] = __builtin_amdgcn_perm(r.w[9], r.w[8], sel);
-  b.qh[1] = __builtin_amdgcn_perm(r.w[10], r.w[9], sel);
-  return b;
-}
-
 // Process blocks [b_begin, b_end) of this workgroup's rows for MC tokens.
 template <bool kBf16, int MC>
 __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint8_t* wexp, int b_begin,
@@ -243,18 +222,8 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   const int valid = max(0, min(kTileRows, a.n - rowbase));
   const uint8_t* tb = wexp + static_cast<int64_t>(min(rowbase, a.n)) * a.nb * kBlockBytes;
   const Rsrc rs = make_rsrc(tb, (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u);
-  typedef int v4i __attribute__((ext_vector_type(4)));
-  typedef int v3i __attribute__((ext_vector_type(3)));
-
-  auto load_w = [&](Raw& r, int b) {
-    const uint32_t off = (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes;
-    const uint32_t o4 = off & ~3u;
-    const v4i p0 = __builtin_amdgcn_raw_buffer_load_b128(rs, o4, 0, 0);
-    const v4i p1 = __builtin_amdgcn_raw_buffer_load_b128(rs, o4 + 16, 0, 0);
-    const v3i p2 = __builtin_amdgcn_raw_buffer_load_b96(rs, o4 + 32, 0, 0);
-    r.w[0] = p0.x; r.w[1] = p0.y; r.w[2] = p0.z; r.w[3] = p0.w;
-    r.w[4] = p1.x; r.w[5] = p1.y; r.w[6] = p1.z; r.w[7] = p1.w;
-    r.w[8] = p2.x; r.w[9] = p2.y; r.w[10] = p2.z;
+  auto load_w = [&](RawBlock& r, int b) {
+    load_raw_block(rs, (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes, r);
   };
   auto load_x = [&](XGroup<kBf16> (&x)[2], int b) {
     const int64_t col = static_cast<int64_t>(b) * kQK + 4 * it_g;
@@ -273,11 +242,11 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   // Pipeline over blocks j = b - b_begin: weights of blocks j, j+1 and
   // activations of blocks j+1, j+2 are in flight; block j uses weight slot
   // j&1, table buffer j&1, and builds table j+1 from activation slot (j+1)&1.
-  Raw wa, wb;
+  RawBlock wa, wb;
   XGroup<kBf16> xa[2], xb[2];
-  auto step = [&](Raw& wcur, XGroup<kBf16> (&xnext)[2], char* tcur, char* tnext, int b) {
+  auto step = [&](RawBlock& wcur, XGroup<kBf16> (&xnext)[2], char* tcur, char* tnext, int b) {
     const bool odd = ((static_cast<uint32_t>(b) * valid) & 1u) ? !lane_odd : lane_odd;
-    const Block blk = realign(wcur, odd);
+    const Block blk = realign_block(wcur, odd);
     if (b + 1 < b_end) build(xnext, tnext);
     if (b + 2 < b_end) load_w(wcur, b + 2);
     if (b + 3 < b_end) load_x(xnext, b + 3);

@@ -35,48 +35,12 @@ __device__ __forceinline__ int64_t block_offset(int r, int b, int n, int nb) {
   return (static_cast<int64_t>(t0) * nb + static_cast<int64_t>(b) * rows + (r - t0)) * kBlockBytes;
 }
 
-// One block unpacked into whole words.  Blocks start at even addresses; the
-// two cases below are the two possible alignments modulo 4.  Every load is
-// 4-byte aligned and stays inside the 4-byte words that hold the block, so
-// it never crosses into a page the block does not touch.
+// One block unpacked into whole words.
 struct Block {
   uint32_t d16;
   uint32_t qs[8];
   uint32_t qh[2];
 };
-
-__device__ __forceinline__ uint32_t funnel16(uint32_t hi, uint32_t lo) {
-  return __builtin_amdgcn_alignbyte(hi, lo, 2);  // (hi:lo) >> 16
-}
-
-// Unpack from 11 consecutive aligned words starting at the word holding the
-// block's first byte; `odd` says the block starts at byte 2 of that word.
-__device__ __forceinline__ Block block_from_words(const uint32_t (&v)[11], bool odd) {
-  Block b;
-  if (odd) {
-    b.d16 = v[0] >> 16;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b.qs[i] = v[i + 1];
-    b.qh[0] = v[9];
-    b.qh[1] = v[10];
-  } else {
-    b.d16 = v[0] & 0xFFFFu;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b.qs[i] = funnel16(v[i + 1], v[i]);
-    b.qh[0] = funnel16(v[9], v[8]);
-    b.qh[1] = funnel16(v[10], v[9]);
-  }
-  return b;
-}
-
-__device__ __forceinline__ Block load_block_global(const uint8_t* p) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
-  uint32_t v[11];
-#pragma unroll
-  for (int i = 0; i < 11; ++i) v[i] = __builtin_nontemporal_load(w + i);
-  return block_from_words(v, (a & 2) != 0);
-}
 
 // Raw buffer access: 32-bit byte offsets against a base and a size; a dword
 // whose offset is at or past the size reads as 0 (gfx9 buffer range check).
@@ -97,13 +61,41 @@ __device__ __forceinline__ uint32_t buf_u32(Rsrc r, uint32_t voff, uint32_t soff
   return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0);
 }
 
-// Block at byte offset `off` (even) of buffer r.
-__device__ __forceinline__ Block load_block_buf(Rsrc r, uint32_t off) {
-  const uint32_t base = off & ~3u;
-  uint32_t v[11];
+// The 11 aligned words that cover one 42-byte block.  A block starts at an
+// even byte; `off & ~3` is the word holding its first byte, and the three
+// loads (16 + 16 + 12 bytes) end at most 2 bytes past the block, inside the
+// word holding its last byte.  Inside a tile run the 64 lanes of a wavefront
+// loading consecutive blocks cover the run with no gaps.
+struct RawBlock {
+  uint32_t w[11];
+};
+
+__device__ __forceinline__ void load_raw_block(Rsrc r, uint32_t off, RawBlock& raw) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  typedef int v3i __attribute__((ext_vector_type(3)));
+  const int o4 = static_cast<int>(off & ~3u);
+  const v4i p0 = __builtin_amdgcn_raw_buffer_load_b128(r, o4, 0, 0);
+  const v4i p1 = __builtin_amdgcn_raw_buffer_load_b128(r, o4 + 16, 0, 0);
+  const v3i p2 = __builtin_amdgcn_raw_buffer_load_b96(r, o4 + 32, 0, 0);
+  raw.w[0] = p0.x; raw.w[1] = p0.y; raw.w[2] = p0.z; raw.w[3] = p0.w;
+  raw.w[4] = p1.x; raw.w[5] = p1.y; raw.w[6] = p1.z; raw.w[7] = p1.w;
+  raw.w[8] = p2.x; raw.w[9] = p2.y; raw.w[10] = p2.z;
+}
+
+// Realign with byte permutes: word i of the block body is bytes 2..5 of
+// (w[i+1]:w[i]) when the block starts on a word boundary, and w[i+1] itself
+// when it starts 2 bytes into w[0] (`odd`); both are one v_perm with a
+// per-thread selector over the same two registers.
+__device__ __forceinline__ Block realign_block(const RawBlock& r, bool odd) {
+  const uint32_t sel = odd ? 0x07060504u : 0x05040302u;
+  const uint32_t seld = odd ? 0x0C0C0302u : 0x0C0C0100u;   // selector byte 0x0C gives 0x00
+  Block b;
+  b.d16 = __builtin_amdgcn_perm(r.w[1], r.w[0], seld);
 #pragma unroll
-  for (int i = 0; i < 11; ++i) v[i] = buf_u32(r, base + 4 * i, 0);
-  return block_from_words(v, (off & 2u) != 0);
+  for (int i = 0; i < 8; ++i) b.qs[i] = __builtin_amdgcn_perm(r.w[i + 1], r.w[i], sel);
+  b.qh[0] = __builtin_amdgcn_perm(r.w[9], r.w[8], sel);
+  b.qh[1] = __builtin_amdgcn_perm(r.w[10], r.w[9], sel);
+  return b;
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
