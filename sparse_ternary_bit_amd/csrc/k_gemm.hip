@@ -19,7 +19,8 @@
 //   * activations of block b+1 for the pass stream from global memory
 //     straight into LDS (16-byte direct loads) into the second of two
 //     buffers; a token's 32 16-byte chunks are stored XOR-swizzled by the
-//     token index so the matrix-operand reads below are bank-conflict free;
+//     token index (mod 16) so the matrix-operand reads below are
+//     bank-conflict free;
 //   * each wavefront's contiguous tile run of block b+1 streams into LDS the
 //     same way; each lane then reads its own row's 42-byte block there,
 //     realigns it and turns it into four 16-byte records, one per MFMA
@@ -75,7 +76,11 @@ struct Smem {
   // its address.
   uint32_t lut[64];
   float dsc[kWaves][kTileRows];           // fp32(d) of each row's current block
-  u32x4_t rec[kWaves][4][4][16];          // [wave][row tile][k quarter][row]
+  // records: word s2 (k-steps 2*s2, 2*s2+1) of quarter q of row r of row tile
+  // i sits at rec[wave][s2][q][i ^ q][r]; both the writers (a row tile's 16
+  // rows per half wave) and the readers (two quarters per half wave) then
+  // touch 32 distinct banks
+  uint32_t rec[kWaves][4][4][4][16];
   alignas(16) char x[2][kXBuf];           // activations, current and next block
   alignas(16) char wraw[kWaves][kWRaw];   // each wavefront's tile run of the next block
 };
@@ -103,19 +108,19 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
   const uint8_t* tb = wexp + static_cast<int64_t>(min(trow0, a.n)) * a.nb * kBlockBytes;
   const Rsrc rs = make_rsrc(tb, (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u);
 
-  // activations: 2 tokens (64 chunks of 16 bytes) per wavefront instruction
+  // activations: 2 tokens (64 chunks of 16 bytes) per wavefront instruction;
+  // chunk c of token t goes to slot c ^ (t & 15) of the token's 512 bytes
   const int n_ins = (mt + 1) >> 1;
-  const int st_t = lane >> 5, st_p = lane & 31;
+  const uint32_t xrow = static_cast<uint32_t>(a.k) * 2;
+  const Rsrc xs_rs = make_rsrc(a.x + row0 * a.k, static_cast<uint32_t>(mt) * xrow);
   auto stage_x = [&](int b, int buf) {
     for (int j = wave; j < n_ins; j += kWaves) {
-      const int t = 2 * j + st_t;
-      const int c = st_p ^ (t & 7);
-      const int tt = min(t, mt - 1);
-      const uint16_t* g = a.x + (row0 + tt) * a.k + static_cast<int64_t>(b) * kQK + 8 * c;
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(g),
-                                       reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                           reinterpret_cast<uintptr_t>(sh.x[buf] + j * 1024)),
-                                       16, 0, 0);
+      const int t = 2 * j + (lane >> 5);
+      const int c = (lane & 31) ^ (t & 15);
+      const uint32_t voff = static_cast<uint32_t>(min(t, mt - 1)) * xrow + static_cast<uint32_t>(b) * kRowBytes + c * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xs_rs, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(sh.x[buf] + j * 1024)),
+          16, static_cast<int>(voff), 0, 0, 0);
     }
   };
 
@@ -155,24 +160,24 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
     }
     // quarter q covers groups 8s+2q, 8s+2q+1 of k-step s: bytes (2q, 2q+1) of
     // cl for q < 2, of cu for q >= 2
-    u32x4_t rq[4];
+    const int ti = lane >> 4, tr = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rq[0][i] = __builtin_amdgcn_perm(cl[2 * i + 1], cl[2 * i], 0x05040100u);
-      rq[1][i] = __builtin_amdgcn_perm(cl[2 * i + 1], cl[2 * i], 0x07060302u);
-      rq[2][i] = __builtin_amdgcn_perm(cu[2 * i + 1], cu[2 * i], 0x05040100u);
-      rq[3][i] = __builtin_amdgcn_perm(cu[2 * i + 1], cu[2 * i], 0x07060302u);
+    for (int s2 = 0; s2 < 4; ++s2) {
+      sh.rec[wave][s2][0][ti ^ 0][tr] = __builtin_amdgcn_perm(cl[2 * s2 + 1], cl[2 * s2], 0x05040100u);
+      sh.rec[wave][s2][1][ti ^ 1][tr] = __builtin_amdgcn_perm(cl[2 * s2 + 1], cl[2 * s2], 0x07060302u);
+      sh.rec[wave][s2][2][ti ^ 2][tr] = __builtin_amdgcn_perm(cu[2 * s2 + 1], cu[2 * s2], 0x05040100u);
+      sh.rec[wave][s2][3][ti ^ 3][tr] = __builtin_amdgcn_perm(cu[2 * s2 + 1], cu[2 * s2], 0x07060302u);
     }
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) sh.rec[wave][lane >> 4][qq][lane & 15] = rq[qq];
     sh.dsc[wave][lane] = half_bits_to_float(blk.d16);
   };
 
 
-  // B operand addresses: token 16*bt + r, chunk (4s + q) ^ (r & 7)
-  const int u = q ^ (r & 7);
-  const int xb_even = r * kRowBytes + u * 16;
-  const int xb_odd = r * kRowBytes + (u ^ 4) * 16;
+  // B operand addresses: token 16*bt + r, chunk 4s + q in slot (4s + q) ^ r,
+  // which is ((4 * (s & 3)) ^ q ^ r) + 16 * (s >> 2)
+  const int u = q ^ r;
+  int xb[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) xb[s4] = r * kRowBytes + ((4 * s4) ^ u) * 16;
 
   const f32x4_t zero4 = {opaque_zero(), opaque_zero(), opaque_zero(), opaque_zero()};
   f32x4_t tot[4][NT];
@@ -204,7 +209,7 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
       bf16x8_t A[4];
       uint32_t Rw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Rw[i] = sh.rec[wave][i][q][r][s >> 1];
+      for (int i = 0; i < 4; ++i) Rw[i] = sh.rec[wave][s >> 1][q][i ^ q][r];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t w = Rw[i];
@@ -217,7 +222,7 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
         v[3] = *reinterpret_cast<const uint32_t*>(lut + c2 + 128);
         A[i] = __builtin_bit_cast(bf16x8_t, v);
       }
-      const int xo = ((s & 1) ? xb_odd + 64 * (s - 1) : xb_even + 64 * s);
+      const int xo = xb[s & 3] + 256 * (s >> 2);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(xs + xo + t * 16 * kRowBytes);
@@ -227,6 +232,8 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
           part[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], B, c, 0, 0, 0);
         }
       }
+      // keep each k-step's operand reads next to its MFMAs (bounded live ranges)
+      __builtin_amdgcn_sched_barrier(0);
     }
     // scale the block's partial sums: rows 16i + 4q + j of the tile
 #pragma unroll
