@@ -41,8 +41,10 @@
  *     returns a status and stq_last_error() holds a message (thread-local);
  *   - STQ_E_HIP means a HIP call failed (launch, allocation); device faults
  *     surface at the caller's next synchronisation;
- *   - stq_gemv keeps a per-device scratch buffer that it grows on demand with
- *     hipMalloc and keeps until the process ends (see stq_gemv).
+ *   - stq_gemv and stq_moe_ffn_decode share a per-device scratch arena that
+ *     grows on demand with hipMalloc and is kept until the process ends;
+ *     calls that may overlap on one device must be issued on one stream from
+ *     one host thread at a time.
  */
 #ifndef STQ_H
 #define STQ_H
@@ -122,12 +124,38 @@ stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, floa
  *   y         [n_pairs, n] fp32
  * Accumulation is fp32 with products exact; the summation order is fixed,
  * so repeated calls give identical bits.  Splitting k across workgroups uses
- * a per-device scratch buffer (grown with hipMalloc on first need and kept);
- * calls that overlap on one device must use the same stream. */
+ * the per-device scratch arena (see the conventions above). */
 stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts,
                     int64_t n, int64_t k, const void* x, int x_dtype, int64_t x_row_stride,
                     int64_t n_tokens, const int32_t* pair_expert, const int32_t* pair_token,
                     int64_t n_pairs, float* y, stq_stream_t stream);
+
+/* Routed-expert FFN of one MoE layer for a batch of decode tokens, its
+ * expert projections in STQ1_0 (lemmy post 66506, paragraph "Runtime": the
+ * routed experts' projections run through STQ1_0 kernels; routing top-k of
+ * the routed experts, traictory.com "Tencent's 200GB Hy4-preview ...",
+ * section "The claim, stated precisely").  For token t and its pairs
+ * p = t*top_k + k, k = 0..top_k-1, with e = pair_expert[p]:
+ *     g, u  = rows [0, d_ff) and [d_ff, 2*d_ff) of W_gate_up[e] x_t
+ *     h     = silu(g) * u,          silu(v) = v / (1 + exp(-v))   (fp32)
+ *     z_p   = W_down[e] h
+ *     y[t]  = sum over k, in order, of pair_weight[p] * z_p        (fp32)
+ *   w_gate_up  expert e's packed [2*d_ff, d_model] matrix (gate rows, then up
+ *              rows) at w_gate_up + e*gate_up_stride_bytes
+ *   w_down     expert e's packed [d_model, d_ff] matrix at w_down + e*down_stride_bytes
+ *              (both 16-byte aligned, strides multiples of 16 and at least
+ *              the packed matrix size; d_model, d_ff multiples of 256)
+ *   x          bf16 bits [n_tokens, d_model], row-major
+ *   pair_expert int32, pair_weight fp32 [n_tokens*top_k], token-major
+ *   y          fp32 [n_tokens, d_model]
+ * Both projections run through the GEMV above (pairs sharing an expert are
+ * batched), the activation inside the down projection's operand load;
+ * intermediates live in the scratch arena.  A pair whose expert is outside
+ * [0, n_experts) makes its token's row NaN.  At most 65535 pairs per call. */
+stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_bytes, const uint8_t* w_down,
+                              int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
+                              const uint16_t* x, int64_t n_tokens, const int32_t* pair_expert,
+                              const float* pair_weight, int64_t top_k, float* y, stq_stream_t stream);
 
 /* Grouped GEMM of the prefill path: tokens routed to each expert,
  * grouped by expert, times that expert's STQ1_0 matrix.

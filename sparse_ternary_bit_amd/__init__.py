@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
     L.stq_gemv.restype = _c_int
     L.stq_grouped_gemm.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
     L.stq_grouped_gemm.restype = _c_int
+    L.stq_moe_ffn_decode.argtypes = [_c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
+                                     _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
+    L.stq_moe_ffn_decode.restype = _c_int
     _lib = L
     return L
 
@@ -181,4 +184,30 @@ def grouped_gemm(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: i
     _check("stq_grouped_gemm", lib().stq_grouped_gemm(w_table.data_ptr(), int(expert_stride), int(n_experts),
                                                       int(n), int(k), x_sorted.data_ptr(), offsets.data_ptr(),
                                                       total_m, out.data_ptr(), _stream()))
+    return out
+
+
+def moe_ffn_decode(w_gate_up: torch.Tensor, gate_up_stride: int, w_down: torch.Tensor, down_stride: int,
+                   n_experts: int, d_model: int, d_ff: int, x: torch.Tensor, pair_expert: torch.Tensor,
+                   pair_weight: torch.Tensor, top_k: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed-expert FFN for decode tokens x bf16 [T, d_model]: per token, the routing-weighted sum
+    over its top_k pairs of W_down_e (silu(W_gate_e x) * (W_up_e x)); pairs token-major [T*top_k]."""
+    _on_gpu("w_gate_up", w_gate_up, torch.uint8)
+    _on_gpu("w_down", w_down, torch.uint8)
+    _on_gpu("x", x, torch.bfloat16)
+    _on_gpu("pair_expert", pair_expert, torch.int32)
+    _on_gpu("pair_weight", pair_weight, torch.float32)
+    n_tokens = x.shape[0]
+    if x.shape[1] != d_model:
+        raise ValueError("x must be [n_tokens, d_model]")
+    if pair_expert.numel() != n_tokens * top_k or pair_weight.numel() != n_tokens * top_k:
+        raise ValueError("pair_expert and pair_weight must hold n_tokens*top_k entries")
+    if out is None:
+        out = torch.empty((n_tokens, d_model), dtype=torch.float32, device=x.device)
+    _on_gpu("out", out, torch.float32)
+    _check("stq_moe_ffn_decode",
+           lib().stq_moe_ffn_decode(w_gate_up.data_ptr(), int(gate_up_stride), w_down.data_ptr(), int(down_stride),
+                                    int(n_experts), int(d_model), int(d_ff), x.data_ptr(), n_tokens,
+                                    pair_expert.data_ptr(), pair_weight.data_ptr(), int(top_k), out.data_ptr(),
+                                    _stream()))
     return out

@@ -66,10 +66,12 @@ struct KArgs {
   int bps;         // blocks per split
   int splits;
   float* partial;  // [splits, n_pairs, n] when splits > 1
+  int ppt;         // without pair_token: pair q uses token q / ppt
+  int64_t ff;      // SwiGLU activations: offset of the "up" half in a row
 };
 
 __device__ __forceinline__ int pair_expert(const KArgs& a, int q) { return a.pe ? a.pe[q] : 0; }
-__device__ __forceinline__ int pair_token(const KArgs& a, int q) { return a.pt ? a.pt[q] : q; }
+__device__ __forceinline__ int pair_token(const KArgs& a, int q) { return a.pt ? a.pt[q] : q / a.ppt; }
 
 struct Shared {
   alignas(16) char tab[2][kBufBytes];       // two table buffers; per token 32 signed sums x 64 groups
@@ -124,12 +126,17 @@ __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
   }
 }
 
-// Activations of one group (4 values) of one token at column `col`.
-template <bool kBf16>
+// Activations of one group (4 values) of one token at column `col`, by
+// source kind: fp32 rows, bf16 rows, or SwiGLU of fp32 gate/up rows
+// (value = silu(row[col]) * row[ff + col], silu(v) = v / (1 + exp(-v))).
+enum XMode { kXF32 = 0, kXBF16 = 1, kXSwiGLU = 2 };
+
+template <int kMode>
 struct XGroup {
-  uint32_t v[kBf16 ? 2 : 4];
+  static constexpr int kWords = kMode == kXBF16 ? 2 : (kMode == kXSwiGLU ? 8 : 4);
+  uint32_t v[kWords];
   __device__ __forceinline__ void load(const KArgs& a, int tok, int64_t col) {
-    if constexpr (kBf16) {
+    if constexpr (kMode == kXBF16) {
       const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.x) + tok * a.xstride + col);
       v[0] = p[0];
       v[1] = p[1];
@@ -137,18 +144,28 @@ struct XGroup {
       const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.x) + tok * a.xstride + col);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = p[i];
+      if constexpr (kMode == kXSwiGLU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 + i] = p[a.ff + i];
+      }
     }
   }
   __device__ __forceinline__ float get(int j) const {
-    if constexpr (kBf16) return __uint_as_float(j & 1 ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16));
-    else return __uint_as_float(v[j]);
+    if constexpr (kMode == kXBF16) {
+      return __uint_as_float(j & 1 ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16));
+    } else if constexpr (kMode == kXSwiGLU) {
+      const float g = __uint_as_float(v[j]);
+      return g / (1.0f + expf(-g)) * __uint_as_float(v[4 + j]);
+    } else {
+      return __uint_as_float(v[j]);
+    }
   }
 };
 
 // Table entries 8z..8z+7 of one group for zero lane z.  Entry 8z+m is the sum
 // over the three kept lanes (in order) of -x or +x as bit r of m says.
-template <bool kBf16>
-__device__ __forceinline__ void build_entries(const XGroup<kBf16>& xg, int z, char* dst) {
+template <int kMode>
+__device__ __forceinline__ void build_entries(const XGroup<kMode>& xg, int z, char* dst) {
   const float x0 = xg.get(0), x1 = xg.get(1), x2 = xg.get(2), x3 = xg.get(3);
   const float a = (z == 0) ? x1 : x0;
   const float b = (z <= 1) ? x2 : x1;
@@ -191,7 +208,7 @@ __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, flo
 }
 
 // Process blocks [b_begin, b_end) of this workgroup's rows for MC tokens.
-template <bool kBf16, int MC>
+template <int kMode, int MC>
 __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint8_t* wexp, int b_begin,
                                           int b_end, float (&acc)[kMT]) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -225,14 +242,14 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   auto load_w = [&](RawBlock& r, int b) {
     load_raw_block(rs, (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes, r);
   };
-  auto load_x = [&](XGroup<kBf16> (&x)[2], int b) {
+  auto load_x = [&](XGroup<kMode> (&x)[2], int b) {
     const int64_t col = static_cast<int64_t>(b) * kQK + 4 * it_g;
     if (has0) x[0].load(a, tok0, col);
     if (has1) x[1].load(a, tok1, col);
   };
-  auto build = [&](const XGroup<kBf16> (&x)[2], char* t) {
-    if (has0) build_entries<kBf16>(x[0], it_z, t + tab_off0);
-    if (has1) build_entries<kBf16>(x[1], it_z, t + tab_off1);
+  auto build = [&](const XGroup<kMode> (&x)[2], char* t) {
+    if (has0) build_entries<kMode>(x[0], it_z, t + tab_off0);
+    if (has1) build_entries<kMode>(x[1], it_z, t + tab_off1);
   };
   // 42*(b*valid + lane) is 2 mod 4 exactly when b*valid + lane is odd
   const bool lane_odd = (lane & 1) != 0;
@@ -243,8 +260,8 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   // activations of blocks j+1, j+2 are in flight; block j uses weight slot
   // j&1, table buffer j&1, and builds table j+1 from activation slot (j+1)&1.
   RawBlock wa, wb;
-  XGroup<kBf16> xa[2], xb[2];
-  auto step = [&](RawBlock& wcur, XGroup<kBf16> (&xnext)[2], char* tcur, char* tnext, int b) {
+  XGroup<kMode> xa[2], xb[2];
+  auto step = [&](RawBlock& wcur, XGroup<kMode> (&xnext)[2], char* tcur, char* tnext, int b) {
     const bool odd = ((static_cast<uint32_t>(b) * valid) & 1u) ? !lane_odd : lane_odd;
     const Block blk = realign_block(wcur, odd);
     if (b + 1 < b_end) build(xnext, tnext);
@@ -256,7 +273,7 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   {
     load_w(wa, b_begin);
     if (b_begin + 1 < b_end) load_w(wb, b_begin + 1);
-    XGroup<kBf16> x0[2];
+    XGroup<kMode> x0[2];
     load_x(x0, b_begin);
     if (b_begin + 1 < b_end) load_x(xb, b_begin + 1);
     if (b_begin + 2 < b_end) load_x(xa, b_begin + 2);
@@ -269,7 +286,7 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   }
 }
 
-template <bool kBf16>
+template <int kMode>
 __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
   __shared__ Shared sh;
   const int tid = threadIdx.x;
@@ -307,10 +324,10 @@ __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
     cursor = __builtin_amdgcn_readfirstlane(sh.next);
     float acc[kMT];
     switch (mc) {
-      case 1: run_chunk<kBf16, 1>(a, sh, wexp, b_begin, b_end, acc); break;
-      case 2: run_chunk<kBf16, 2>(a, sh, wexp, b_begin, b_end, acc); break;
-      case 3: run_chunk<kBf16, 3>(a, sh, wexp, b_begin, b_end, acc); break;
-      default: run_chunk<kBf16, 4>(a, sh, wexp, b_begin, b_end, acc); break;
+      case 1: run_chunk<kMode, 1>(a, sh, wexp, b_begin, b_end, acc); break;
+      case 2: run_chunk<kMode, 2>(a, sh, wexp, b_begin, b_end, acc); break;
+      case 3: run_chunk<kMode, 3>(a, sh, wexp, b_begin, b_end, acc); break;
+      default: run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc); break;
     }
     if (row_ok) {
 #pragma unroll
@@ -329,13 +346,13 @@ __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
 // y[p, r] = sum over splits s, in order, of partial[s, p, r], for valid pairs.
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partial, int splits,
                                                             int64_t plane, const int32_t* __restrict__ pe,
-                                                            const int32_t* __restrict__ pt, int n_experts,
+                                                            const int32_t* __restrict__ pt, int ppt, int n_experts,
                                                             int n_tokens, int n, float* __restrict__ y) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= plane) return;
   const int p = static_cast<int>(i / n);
   const int e = pe ? pe[p] : 0;
-  const int t = pt ? pt[p] : p;
+  const int t = pt ? pt[p] : p / ppt;
   if (e < 0 || e >= n_experts || t < 0 || t >= n_tokens) return;  // the GEMV wrote NaN there
   float s = 0.0f;
   for (int sp = 0; sp < splits; ++sp) s += partial[static_cast<int64_t>(sp) * plane + i];
@@ -357,11 +374,10 @@ GemvPlan plan_gemv(const GemvArgs& a) {
   pl.blocks_per_split = bps;
   pl.splits = (nb + bps - 1) / bps;
   if (pl.splits > 1) pl.partial_bytes = static_cast<int64_t>(pl.splits) * a.n_pairs * a.n * 4;
-  pl.counter_bytes = 0;
   return pl;
 }
 
-hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* /*counters*/, void* partial, hipStream_t s) {
+hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hipStream_t s) {
   if (ga.n_pairs == 0 || ga.n == 0) return hipSuccess;
   KArgs a{};
   a.w = ga.w_table;
@@ -379,16 +395,21 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* /*counters*
   a.bps = pl.blocks_per_split;
   a.splits = pl.splits;
   a.partial = static_cast<float*>(partial);
+  a.ppt = ga.pairs_per_token > 0 ? static_cast<int>(ga.pairs_per_token) : 1;
+  a.ff = ga.ff;
   const int ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
   const dim3 grid(ntiles, pl.splits, a.n_pairs);
-  if (ga.x_bf16) hipLaunchKernelGGL((gemv_kernel<true>), grid, dim3(kRows), 0, s, a);
-  else hipLaunchKernelGGL((gemv_kernel<false>), grid, dim3(kRows), 0, s, a);
+  switch (ga.x_mode) {
+    case kXBF16: hipLaunchKernelGGL((gemv_kernel<kXBF16>), grid, dim3(kRows), 0, s, a); break;
+    case kXSwiGLU: hipLaunchKernelGGL((gemv_kernel<kXSwiGLU>), grid, dim3(kRows), 0, s, a); break;
+    default: hipLaunchKernelGGL((gemv_kernel<kXF32>), grid, dim3(kRows), 0, s, a); break;
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || pl.splits == 1) return err;
   const int64_t plane = ga.n_pairs * ga.n;
   const int64_t grid2 = (plane + 255) / 256;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3(static_cast<unsigned>(grid2)), dim3(256), 0, s, a.partial,
-                     pl.splits, plane, a.pe, a.pt, a.n_experts, a.n_tokens, a.n, a.y);
+                     pl.splits, plane, a.pe, a.pt, a.ppt, a.n_experts, a.n_tokens, a.n, a.y);
   return hipGetLastError();
 }
 

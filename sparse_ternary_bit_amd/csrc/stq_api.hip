@@ -39,15 +39,43 @@ stq_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Per-device scratch of stq_gemv: [counters | partial sums].  The counter
-// part is zeroed when allocated and the kernels leave it zeroed.
-struct Scratch {
+// Per-device scratch arena for split-k partial sums and the FFN's
+// intermediates: grown with hipMalloc when a call needs more (hipFree of the
+// old arena waits for work that may still use it) and kept until the
+// process ends.
+struct Arena {
   void* ptr = nullptr;
-  int64_t counter_cap = 0;
-  int64_t partial_cap = 0;
+  int64_t cap = 0;
 };
-std::mutex g_scratch_mu;
-std::unordered_map<int, Scratch> g_scratch;
+std::mutex g_arena_mu;
+std::unordered_map<int, Arena> g_arena;
+
+stq_status arena_get(int64_t bytes, void** out, const char* who) {
+  *out = nullptr;
+  if (bytes <= 0) return STQ_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, who);
+  std::lock_guard<std::mutex> lk(g_arena_mu);
+  Arena& a = g_arena[dev];
+  if (a.cap < bytes) {
+    if (a.ptr) {
+      e = hipFree(a.ptr);
+      a.ptr = nullptr;
+      a.cap = 0;
+      if (e != hipSuccess) return hip_fail(e, who);
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, static_cast<size_t>(bytes));
+    if (e != hipSuccess) return hip_fail(e, who);
+    a.ptr = p;
+    a.cap = bytes;
+  }
+  *out = a.ptr;
+  return STQ_OK;
+}
+
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -118,44 +146,60 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
   if (x_dtype == STQ_X_BF16 && (x_row_stride % 2)) return fail(STQ_E_ALIGN, "stq_gemv: bf16 x_row_stride must be even");
 
   stq::GemvArgs ga{w_table, expert_stride_bytes, n_experts, n, k, x, x_dtype == STQ_X_BF16 ? 1 : 0,
-                   x_row_stride, n_tokens, pair_expert, pair_token, n_pairs, y};
+                   x_row_stride, n_tokens, pair_expert, pair_token, n_pairs, y, 1, 0};
   const stq::GemvPlan pl = stq::plan_gemv(ga);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  void* scratch = nullptr;
-  if (pl.splits > 1) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "stq_gemv: hipGetDevice");
-    std::lock_guard<std::mutex> lk(g_scratch_mu);
-    Scratch& sc = g_scratch[dev];
-    if (sc.counter_cap < pl.counter_bytes || sc.partial_cap < pl.partial_bytes) {
-      const int64_t cc = std::max(sc.counter_cap, pl.counter_bytes);
-      const int64_t pc = std::max(sc.partial_cap, pl.partial_bytes);
-      if (sc.ptr) {
-        e = hipFree(sc.ptr);  // waits for work that may still use it
-        sc.ptr = nullptr;
-        sc.counter_cap = sc.partial_cap = 0;
-        if (e != hipSuccess) return hip_fail(e, "stq_gemv: hipFree scratch");
-      }
-      void* p = nullptr;
-      e = hipMalloc(&p, static_cast<size_t>(cc + pc));
-      if (e != hipSuccess) return hip_fail(e, "stq_gemv: hipMalloc scratch");
-      e = hipMemset(p, 0, static_cast<size_t>(cc));
-      if (e != hipSuccess) {
-        (void)hipFree(p);
-        return hip_fail(e, "stq_gemv: zeroing scratch counters");
-      }
-      sc.ptr = p;
-      sc.counter_cap = cc;
-      sc.partial_cap = pc;
-    }
-    scratch = sc.ptr;
-    hipError_t le = stq::launch_gemv(ga, pl, static_cast<char*>(scratch), static_cast<char*>(scratch) + sc.counter_cap, s);
-    if (le != hipSuccess) return hip_fail(le, "stq_gemv launch");
-    return ok();
-  }
-  hipError_t le = stq::launch_gemv(ga, pl, nullptr, nullptr, s);
+  void* partial = nullptr;
+  const stq_status st = arena_get(pl.splits > 1 ? pl.partial_bytes : 0, &partial, "stq_gemv: scratch");
+  if (st != STQ_OK) return st;
+  hipError_t le = stq::launch_gemv(ga, pl, partial, reinterpret_cast<hipStream_t>(stream));
   if (le != hipSuccess) return hip_fail(le, "stq_gemv launch");
+  return ok();
+}
+
+stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_bytes, const uint8_t* w_down,
+                              int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
+                              const uint16_t* x, int64_t n_tokens, const int32_t* pair_expert,
+                              const float* pair_weight, int64_t top_k, float* y, stq_stream_t stream) {
+  if (n_experts < 1 || n_tokens < 0 || top_k < 1) return fail(STQ_E_ARG, "stq_moe_ffn_decode: bad count (n_experts >= 1, n_tokens >= 0, top_k >= 1)");
+  if (d_model <= 0 || d_model % STQ_QK || d_ff <= 0 || d_ff % STQ_QK)
+    return fail(STQ_E_SHAPE, "stq_moe_ffn_decode: d_model and d_ff must be positive multiples of 256");
+  if (d_model > INT_MAX / 2 || 2 * d_ff > INT_MAX || n_experts > INT_MAX) return fail(STQ_E_SHAPE, "stq_moe_ffn_decode: size exceeds int32");
+  if (n_tokens > 65535 / top_k) return fail(STQ_E_SHAPE, "stq_moe_ffn_decode: more than 65535 (token, expert) pairs");
+  if (gate_up_stride_bytes < 2 * d_ff * stq_row_bytes(d_model) || down_stride_bytes < d_model * stq_row_bytes(d_ff))
+    return fail(STQ_E_SHAPE, "stq_moe_ffn_decode: expert stride smaller than the packed matrix");
+  if (n_tokens == 0) return ok();
+  if (!w_gate_up || !w_down || !x || !pair_expert || !pair_weight || !y) return fail(STQ_E_ARG, "stq_moe_ffn_decode: null pointer");
+  if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || gate_up_stride_bytes % 16 || down_stride_bytes % 16)
+    return fail(STQ_E_ALIGN, "stq_moe_ffn_decode: tables / strides not 16-byte aligned");
+  if (!aligned(x, 4) || !aligned(pair_expert, 4) || !aligned(pair_weight, 4) || !aligned(y, 4))
+    return fail(STQ_E_ALIGN, "stq_moe_ffn_decode: x, pair arrays or y not 4-byte aligned");
+
+  const int64_t P = n_tokens * top_k;
+  // gate/up GEMV of every pair's token, then the down GEMV of SwiGLU(gate/up row)
+  stq::GemvArgs g1{w_gate_up, gate_up_stride_bytes, n_experts, 2 * d_ff, d_model, x, 1, d_model, n_tokens,
+                   pair_expert, nullptr, P, nullptr, top_k, 0};
+  stq::GemvArgs g2{w_down, down_stride_bytes, n_experts, d_model, d_ff, nullptr, 2, 2 * d_ff, P,
+                   pair_expert, nullptr, P, nullptr, 1, d_ff};
+  const stq::GemvPlan p1 = stq::plan_gemv(g1), p2 = stq::plan_gemv(g2);
+  const int64_t part = round256(std::max(p1.splits > 1 ? p1.partial_bytes : 0, p2.splits > 1 ? p2.partial_bytes : 0));
+  const int64_t gu_bytes = round256(P * 2 * d_ff * 4);
+  const int64_t z_bytes = round256(P * d_model * 4);
+  void* base = nullptr;
+  const stq_status st = arena_get(part + gu_bytes + z_bytes, &base, "stq_moe_ffn_decode: scratch");
+  if (st != STQ_OK) return st;
+  char* b = static_cast<char*>(base);
+  float* gu = reinterpret_cast<float*>(b + part);
+  float* z = reinterpret_cast<float*>(b + part + gu_bytes);
+  g1.y = gu;
+  g2.x = gu;
+  g2.y = z;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = stq::launch_gemv(g1, p1, b, s);
+  if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: gate/up launch");
+  e = stq::launch_gemv(g2, p2, b, s);
+  if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: down launch");
+  e = stq::launch_combine(z, pair_weight, n_tokens, top_k, d_model, y, s);
+  if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: combine launch");
   return ok();
 }
 

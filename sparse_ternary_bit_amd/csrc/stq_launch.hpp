@@ -19,27 +19,30 @@ struct GemvArgs {
   int64_t n;
   int64_t k;
   const void* x;
-  int x_bf16;
-  int64_t x_row_stride;
+  int x_mode;               // 0 fp32 rows, 1 bf16 rows, 2 SwiGLU of fp32 gate/up rows
+  int64_t x_row_stride;     // elements
   int64_t n_tokens;
   const int32_t* pair_expert;
-  const int32_t* pair_token;
+  const int32_t* pair_token;  // NULL: pair q uses token q / pairs_per_token
   int64_t n_pairs;
   float* y;
+  int64_t pairs_per_token;  // used only without pair_token (0 means 1)
+  int64_t ff;               // x_mode 2: column offset of the "up" half of a row
 };
 
 // Scratch needed by launch_gemv for the chosen k split (bytes, 0 if none),
-// and the launch itself.  With splits > 1, `counters` must hold counter_bytes
-// zero bytes (the kernels leave them zero when they finish) and `partial`
-// partial_bytes bytes.
+// and the launch itself; with splits > 1, `partial` holds partial_bytes bytes.
 struct GemvPlan {
   int splits;          // k split across workgroups
   int blocks_per_split;
   int64_t partial_bytes;
-  int64_t counter_bytes;
 };
 GemvPlan plan_gemv(const GemvArgs& a);
-hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& plan, void* counters, void* partial, hipStream_t s);
+hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& plan, void* partial, hipStream_t s);
+
+// y[t, :] = sum over k < top_k, in order, of w[t*top_k + k] * z[t*top_k + k, :]
+hipError_t launch_combine(const float* z, const float* w, int64_t n_tokens, int64_t top_k, int64_t n, float* y,
+                          hipStream_t s);
 
 struct GemmArgs {
   const uint8_t* w_table;

@@ -16,6 +16,8 @@ import synth_inputs as S
 N_EXPERTS = 256
 N_ROWS = 4096      # gate + up rows of one expert (2 x 2048)
 K = 7168
+D_FF = N_ROWS // 2  # down projection: [K, D_FF] per expert
+DOWN_SEED = 3000
 TOP_K = 8
 TABLE_SEED = 2000
 IMATRIX_SEED = 3
@@ -46,6 +48,13 @@ def encode_table(n_experts: int = N_EXPERTS, n: int = N_ROWS, k: int = K, seed: 
         stq.quantize_rows(w, imatrix, encoder=encoder, rounds=rounds, out=out)
         del w
     return table, stride
+
+
+def encode_down_table(n_experts: int = N_EXPERTS, d_model: int = K, d_ff: int = D_FF, seed: int = DOWN_SEED,
+                      device="cuda") -> tuple[torch.Tensor, int]:
+    """Down projections [d_model, d_ff] of every expert, drawn like the gate/up table
+    (N(0, 0.02), no imatrix), encoded by the library with 3 WLS rounds."""
+    return encode_table(n_experts, d_model, d_ff, seed=seed, imatrix=None, device=device)
 
 
 def expert_weight_rows(seed: int, expert: int, rows, n: int = N_ROWS, k: int = K, device="cuda") -> np.ndarray:

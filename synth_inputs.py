@@ -97,6 +97,14 @@ def uniform_topk_pairs(seed: int, n_tokens: int, n_experts: int = 256, top_k: in
     return pair_expert, pair_token
 
 
+def routing_weights(seed: int, n_tokens: int, top_k: int = 8) -> np.ndarray:
+    """Decode routing weights, fp32 [n_tokens*top_k] token-major: per token the
+    softmax of top_k N(0,1) draws (positive, summing to 1)."""
+    z = np.random.default_rng(seed).normal(0.0, 1.0, size=(n_tokens, top_k))
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32).reshape(-1)
+
+
 def prefill_routing(seed: int, n_tokens: int, n_experts: int = 256, top_k: int = 8):
     """Prefill routing: router logits N(0,1); softmax top-k (= top-k of the logits).
 

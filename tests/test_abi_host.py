@@ -28,7 +28,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for want in ("stq_quantize_rows", "stq_gemv", "stq_grouped_gemm", "stq_dequantize_rows",
-                 "stq_row_bytes", "stq_status_string", "stq_last_error"):
+                 "stq_moe_ffn_decode", "stq_row_bytes", "stq_status_string", "stq_last_error"):
         assert want in names
 
 
@@ -118,3 +118,30 @@ def test_grouped_gemm_rejects_bad_arguments(L):
     assert g(stride=10) == 2
     assert g(m=-1) == 1
     assert g(m=0, w=None, x=None, y=None) == 0
+
+
+def test_moe_ffn_rejects_bad_arguments(L):
+    gu_stride, dn_stride = 4096 * 1176, 7168 * 336
+
+    def f(**kw):
+        a = dict(wg=FAKE, gs=gu_stride, wd=FAKE, ds=dn_stride, ne=256, dm=7168, ff=2048, x=FAKE, t=4,
+                 pe=FAKE, pw=FAKE, k=8, y=FAKE)
+        a.update(kw)
+        L.stq_moe_ffn_decode.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+        return L.stq_moe_ffn_decode(a["wg"], a["gs"], a["wd"], a["ds"], a["ne"], a["dm"], a["ff"], a["x"], a["t"],
+                                    a["pe"], a["pw"], a["k"], a["y"], None)
+    assert f(dm=7000) == 2
+    assert f(ff=100) == 2
+    assert f(k=0) == 1
+    assert f(ne=0) == 1
+    assert f(gs=10) == 2
+    assert f(ds=dn_stride - 16) == 2
+    assert f(t=10000) == 2            # more than 65535 pairs
+    assert f(pw=None) == 1
+    assert f(wd=FAKE + 4) == 3
+    assert f(gs=gu_stride + 8) == 3
+    assert f(x=FAKE + 2) == 3
+    assert f(t=0, wg=None, wd=None, x=None, pe=None, pw=None, y=None) == 0
