@@ -7,7 +7,10 @@ One step is one pass of the hot path over one batch of synthetic input:
     uniform top-8 routing, on the WLS-encoded table and on an amax-encoded
     table of the same weights (kernel speed must not depend on the encoder);
   * prefill: the grouped GEMM of 2048 tokens routed top-8 (16384 rows grouped
-    by expert) against the same table.
+    by expert) against the same table;
+  * the routed-expert FFN of the layer for decode (gate/up GEMV, SiLU(gate) *
+    up, down GEMV against a 256 x 7168 x 2048 down table, routing combine) at
+    batch 1, 16, 64, reported beside the headline as `moe_ffn_decode`.
 Inputs are resident in HBM before timing starts.  `value` is the GEMV's
 effective bandwidth over the sweep: algorithmic bytes (each touched expert's
 packed bytes once, plus activations and outputs) divided by GEMV time.
@@ -37,6 +40,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 BATCHES = (1, 4, 16, 64)
+FFN_BATCHES = (1, 16, 64)
 PREFILL_TOKENS = 2048
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 COPY_MIB = 512               # plain copy used to calibrate the byte counters
@@ -177,6 +181,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--single-expert", action="store_true",
                     help="also time the batch-1 single-expert GEMV over 100 resident experts")
+    ap.add_argument("--no-ffn", action="store_true",
+                    help="skip the routed-expert FFN lines (profiling runs of the GEMV and GEMM alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"after timing, copy {COPY_MIB} MiB device to device {COPY_REPS} times (counter calibration)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -213,6 +219,8 @@ def main() -> int:
     t_wls, stride = W.encode_table(imatrix=q, encoder=stq.ENC_WLS, device=dev)
     t_amax, _ = W.encode_table(imatrix=q, encoder=stq.ENC_AMAX, device=dev)
     tables = {"wls": t_wls, "amax": t_amax}
+    t_down, down_stride = W.encode_down_table(device=dev)
+    down_bytes = W.K * stq.row_bytes(W.D_FF)
 
     total_steps = args.warmup + args.steps
     sweep = []   # per step: list of (batch, pe, pt, x, y, algorithmic bytes)
@@ -225,6 +233,16 @@ def main() -> int:
             uniq = len(np.unique(pe))
             nbytes = uniq * expert_bytes + B * K * 2 + B * W.TOP_K * N * 4
             items.append((B, pe_t, pt_t, x, y, nbytes, uniq))
+        ffn = []
+        for B in FFN_BATCHES:
+            pe_t, _, pe, _ = W.decode_pairs(70000 + 1000 * s + B, B, device=dev)
+            pw = torch.from_numpy(S.routing_weights(80000 + 1000 * s + B, B, W.TOP_K)).to(dev)
+            x = S.torch_bf16_normal(60000 + 1000 * s + B, (B, K), device=dev)
+            y = torch.empty((B, K), dtype=torch.float32, device=dev)
+            uniq = len(np.unique(pe))
+            nbytes = uniq * (expert_bytes + down_bytes) + B * K * 2 + B * K * 4
+            ffn.append((B, pe_t, pw, x, y, nbytes))
+        items = (items, ffn)
         sweep.append(items)
     x_sorted, offsets_t, _, offsets = W.prefill_batch(PREFILL_TOKENS, K, device=dev)
     total_m = int(offsets[-1])
@@ -244,7 +262,7 @@ def main() -> int:
 
     def run_step(s, rec):
         for enc in ("wls", "amax"):
-            for (B, pe_t, pt_t, x, y, nbytes, uniq) in sweep[s]:
+            for (B, pe_t, pt_t, x, y, nbytes, uniq) in sweep[s][0]:
                 a, b = ev(), ev()
                 a.record(stream)
                 stq.gemv(tables[enc], stride, E, N, K, x, pe_t, pt_t, out=y)
@@ -255,6 +273,12 @@ def main() -> int:
         stq.grouped_gemm(t_wls, stride, E, N, K, x_sorted, offsets_t, out=y_pre)
         b.record(stream)
         rec["gemm"].append((a, b))
+        for (B, pe_t, pw, x, y, nbytes) in ([] if args.no_ffn else sweep[s][1]):
+            a, b = ev(), ev()
+            a.record(stream)
+            stq.moe_ffn_decode(t_wls, stride, t_down, down_stride, E, K, W.D_FF, x, pe_t, pw, W.TOP_K, out=y)
+            b.record(stream)
+            rec["ffn"].append((B, nbytes, a, b))
         if args.single_expert:
             for i in range(100):
                 a, b = ev(), ev()
@@ -264,10 +288,10 @@ def main() -> int:
                 rec["single"].append((a, b))
 
     for s in range(args.warmup):
-        run_step(s, {"gemv": [], "gemm": [], "single": []})
+        run_step(s, {"gemv": [], "gemm": [], "single": [], "ffn": []})
     torch.cuda.synchronize()
 
-    rec = {"gemv": [], "gemm": [], "single": []}
+    rec = {"gemv": [], "gemm": [], "single": [], "ffn": []}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.warmup, total_steps):
@@ -334,6 +358,15 @@ def main() -> int:
                           "flop_per_launch": gemm_flop, "avg_launch_us": round(1e3 * gemm_avg, 1)},
         "gemv_sweep": per_batch,
     }
+    ffn = {}
+    for B in ([] if args.no_ffn else FFN_BATCHES):
+        sel = [(nb, a.elapsed_time(b)) for (b_, nb, a, b) in rec["ffn"] if b_ == B]
+        ms = sum(t for _, t in sel)
+        ffn[f"b{B}"] = {"us": round(1e3 * ms / len(sel), 2),
+                        "GB/s": round(sum(nb for nb, _ in sel) / (ms * 1e-3) / 1e9, 1)}
+    if ffn:
+        out["moe_ffn_decode"] = {"layer": "256 experts, top-8, gate/up 4096x7168 + down 7168x2048, STQ1_0",
+                                 "bytes": "touched experts' packed gate/up and down matrices, x and y", **ffn}
     if rec["single"]:
         sm = [a.elapsed_time(b) for (a, b) in rec["single"]]
         sb = expert_bytes + K * 2 + N * 4
