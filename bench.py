@@ -10,7 +10,10 @@ One step is one pass of the hot path over one batch of synthetic input:
     by expert) against the same table;
   * the routed-expert FFN of the layer for decode (gate/up GEMV, SiLU(gate) *
     up, down GEMV against a 256 x 7168 x 2048 down table, routing combine) at
-    batch 1, 16, 64, reported beside the headline as `moe_ffn_decode`.
+    batch 1, 16, 64, reported beside the headline as `moe_ffn_decode`;
+  * the encoder as a layer-scale workload (`encode_layer`): both encoders on
+    8 experts' fp32 gate/up weights drawn beforehand, extrapolated to the
+    256-expert layer.
 Inputs are resident in HBM before timing starts.  `value` is the GEMV's
 effective bandwidth over the sweep: algorithmic bytes (each touched expert's
 packed bytes once, plus activations and outputs) divided by GEMV time.
@@ -41,6 +44,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 BATCHES = (1, 4, 16, 64)
 FFN_BATCHES = (1, 16, 64)
+ENCODE_EXPERTS = 8
 PREFILL_TOKENS = 2048
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 COPY_MIB = 512               # plain copy used to calibrate the byte counters
@@ -181,6 +185,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--single-expert", action="store_true",
                     help="also time the batch-1 single-expert GEMV over 100 resident experts")
+    ap.add_argument("--no-encode", action="store_true",
+                    help="skip the timed layer-scale encode (8 experts, both encoders)")
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the routed-expert FFN lines (profiling runs of the GEMV and GEMM alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -307,6 +313,28 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    enc_out = None
+    if not args.no_encode:
+        # encoder as a layer-scale workload: 8 experts' fp32 gate/up weights drawn
+        # beforehand, then only the quantize launches are timed
+        ws = [S.torch_expert_weights(W.TABLE_SEED, e, N, K, device=dev) for e in range(ENCODE_EXPERTS)]
+        outq = torch.empty(N * rb, dtype=torch.uint8, device=dev)
+        enc_out = {}
+        for name, enc in (("wls", stq.ENC_WLS), ("amax", stq.ENC_AMAX)):
+            stq.quantize_rows(ws[0], q if enc == stq.ENC_WLS else None, encoder=enc, out=outq)  # warm
+            a, b = ev(), ev()
+            a.record(stream)
+            for w_e in ws:
+                stq.quantize_rows(w_e, q if enc == stq.ENC_WLS else None, encoder=enc, rounds=3, out=outq)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / len(ws)
+            enc_out[name] = {"ms_per_expert": round(ms, 4),
+                             "layer_ms": round(ms * E, 1),
+                             "Gweights_per_s": round(N * K / (ms * 1e-3) / 1e9, 1),
+                             "fp32_read_GB/s": round(N * K * 4 / (ms * 1e-3) / 1e9, 1)}
+        del ws, outq
+
     # ---------------- results ----------------
     gemv_ms = [a.elapsed_time(b) for (_, _, _, _, a, b) in rec["gemv"]]
     gemv_bytes = [nb for (_, _, nb, _, _, _) in rec["gemv"]]
@@ -364,6 +392,10 @@ def main() -> int:
         ms = sum(t for _, t in sel)
         ffn[f"b{B}"] = {"us": round(1e3 * ms / len(sel), 2),
                         "GB/s": round(sum(nb for nb, _ in sel) / (ms * 1e-3) / 1e9, 1)}
+    if enc_out:
+        out["encode_layer"] = {"experts_timed": ENCODE_EXPERTS,
+                               "weights_per_expert": N * K,
+                               "rounds": 3, **enc_out}
     if ffn:
         out["moe_ffn_decode"] = {"layer": "256 experts, top-8, gate/up 4096x7168 + down 7168x2048, STQ1_0",
                                  "bytes": "touched experts' packed gate/up and down matrices, x and y", **ffn}

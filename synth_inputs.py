@@ -72,6 +72,17 @@ def calibration_imatrix(seed: int, n_vec: int, k: int) -> np.ndarray:
     return imatrix_from_calibration(np.random.default_rng(seed).normal(0.0, 1.0, size=(n_vec, k)))
 
 
+def heavy_tailed_imatrix(seed: int, n_vec: int, k: int, frac: float = 0.02, scale: float = 30.0) -> np.ndarray:
+    """Importance from calibration vectors with outlier channels: a random
+    `frac` of the k input channels have activations `scale` times larger
+    (N(0, scale^2) instead of N(0, 1)), as in the activation outliers that
+    make some input columns dominate the weighted error."""
+    rng = np.random.default_rng(seed)
+    sigma = np.ones(k)
+    sigma[rng.choice(k, max(1, int(round(frac * k))), replace=False)] = scale
+    return imatrix_from_calibration(rng.normal(0.0, 1.0, size=(n_vec, k)) * sigma)
+
+
 # ----------------------------------------------------------------------------
 # named workloads
 # ----------------------------------------------------------------------------

@@ -109,6 +109,16 @@ def test_quantize_bit_exact_varied(stq, case, encoder):
     assert np.array_equal(got, want), name
 
 
+@pytest.mark.parametrize("rounds", [0, 1, 3, 5])
+def test_quantize_bit_exact_heavy_tailed_imatrix(stq, rounds):
+    """Outlier-channel importance, where the rounds move many zeros away from
+    the smallest |w|: still byte-identical to the oracle."""
+    w = S.gaussian_weights(0, 256, 1024)
+    q = S.heavy_tailed_imatrix(1, 64, 1024)
+    got = host(stq.quantize_rows(dev(w), dev(q), encoder=stq.ENC_WLS, rounds=rounds))
+    assert np.array_equal(got, O.quantize_rows(w, q, rounds=rounds))
+
+
 # ---------------------------------------------------------------------------
 # GEMV
 # ---------------------------------------------------------------------------
