@@ -344,6 +344,8 @@ __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
 }
 
 // y[p, r] = sum over splits s, in order, of partial[s, p, r], for valid pairs.
+// The loads of 16 splits are issued before their adds, so the loop pays one
+// memory latency per 16 splits; the additions stay in split order.
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partial, int splits,
                                                             int64_t plane, const int32_t* __restrict__ pe,
                                                             const int32_t* __restrict__ pt, int ppt, int n_experts,
@@ -354,8 +356,23 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   const int e = pe ? pe[p] : 0;
   const int t = pt ? pt[p] : p / ppt;
   if (e < 0 || e >= n_experts || t < 0 || t >= n_tokens) return;  // the GEMV wrote NaN there
+  constexpr int kBatch = 16;
   float s = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) s += partial[static_cast<int64_t>(sp) * plane + i];
+  int sp = 0;
+  for (; sp + kBatch <= splits; sp += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = partial[static_cast<int64_t>(sp + j) * plane + i];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) s += v[j];
+  }
+  float v[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    if (sp + j < splits) v[j] = partial[static_cast<int64_t>(sp + j) * plane + i];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    if (sp + j < splits) s += v[j];
   y[i] = s;
 }
 
