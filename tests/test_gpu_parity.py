@@ -264,6 +264,20 @@ def test_grouped_gemm_against_oracle(stq, k, n):
     _check_grouped(y, table, stride, n, k, xf, offsets)
 
 
+@pytest.mark.parametrize("k,n", [(256, 130), (16384, 72)])
+def test_grouped_gemm_pass_boundaries(stq, k, n):
+    """Token counts at and around the 16-token tile and the 80-token pass
+    (16, 17, 80, 81, 200 = three passes), empty experts in between; n not a
+    multiple of 4 or 64 (scalar stores, partial tiles); k of 1 and 64 blocks."""
+    counts = [16, 0, 17, 80, 0, 81, 200, 1]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    table, stride = _grouped_case(k, n, offsets, 600)
+    xb, xf = S.bf16_normal(np.random.default_rng(k + n), (int(offsets[-1]), k))
+    y = host(stq.grouped_gemm(dev(table), stride, len(counts), n, k,
+                              dev(xb.view(np.int16)).view(torch.bfloat16), dev(offsets)))
+    _check_grouped(y, table, stride, n, k, xf, offsets)
+
+
 def test_grouped_gemm_exact_special_inputs(stq):
     k, n = 768, 160
     rng = np.random.default_rng(3)
