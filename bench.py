@@ -406,6 +406,27 @@ def main() -> int:
                                      "us_p10": round(1e3 * float(np.percentile(sm, 10)), 2),
                                      "us_p90": round(1e3 * float(np.percentile(sm, 90)), 2),
                                      "GB/s_median": round(sb / (float(np.median(sm)) * 1e-3) / 1e9, 1)}
+        # the same 100 calls captured once into a HIP graph and replayed: a
+        # decode loop's per-call cost without host launch gaps
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(100):
+                    stq.gemv(t_wls, stride, E, N, K, xs1[i], pes1[i], out=ys1)
+        torch.cuda.current_stream().wait_stream(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(5):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per = a.elapsed_time(b) / 500
+        out["single_expert_gemv"]["graph_us_per_call"] = round(1e3 * per, 2)
+        out["single_expert_gemv"]["graph_GB/s"] = round(sb / (per * 1e-3) / 1e9, 1)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out))
