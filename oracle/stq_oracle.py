@@ -517,3 +517,86 @@ def moe_ffn_tolerance(gate_up: dict, down: dict, d_model: int, d_ff: int, x: np.
         else:
             bound[t] = acc_dz + top_k * eps_sum * acc_mag
     return bound
+
+
+# -----------------------------------------------------------------------------
+# Layer sensitivity and mixed-precision allocation ([LEMMY] "Full-Hessian
+# scoring"; [AGI] "Four weights, five bits" on the per-layer mix).  The pages:
+# sensitivity is measured with the full Hessian H = X X^T of the layer's
+# calibration activations, whose off-diagonal terms the diagonal imatrix
+# misses; layers are chosen greedily by error reduction per added byte, the
+# alternative to STQ1_0 being a ~2-bit format (IQ2_XXS, not described on the
+# pages).  Readings: the error of a quantized layer is ||(W - W_hat) X^T||_F^2
+# over calibration rows X [N, k] (full) or sum_k (sum_i x_ik^2) (W - W_hat)_k^2
+# (diagonal); the stand-in ~2-bit format is Q2 below.
+# -----------------------------------------------------------------------------
+Q2_BLOCK_BYTES = 66      # fp16 scale + 256 x 2-bit levels: 2.0625 bits per weight
+
+
+def q2_roundtrip(w: np.ndarray) -> np.ndarray:
+    """Stand-in 2-bit format: per 256 weights one scale s = rms/2 (rms = root
+    mean square of the block, fp64; stored as fp16 via fp32, nearest-even,
+    clamped to 65504) and levels {-3,-1,+1,+3}*s, each weight taking the
+    nearest level (ties to the larger magnitude; the sign is the sign bit of w,
+    so -0.0 maps to -s).  For Gaussian
+    weights the levels sit near the minimum-error 4-level points (about
+    +-0.45 and +-1.5 standard deviations).  Returns the reconstruction (fp32)."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    b = w.reshape(n, k // QK, QK // GROUP, GROUP).astype(np.float64)
+    # sum of squares in the encoder's fixed order (lanes of a group, then the
+    # balanced tree of adjacent groups), so the stored scale is unique
+    ss = _tree_sum(_group_partial(b * b))
+    rms = np.sqrt(ss / QK)
+    s16 = np.minimum(rms / 2.0, FP16_MAX).astype(np.float32).astype(np.float16).astype(np.float64)
+    s = s16[..., None, None]
+    a = np.abs(b)
+    mag = np.where(a < 2.0 * s, s, 3.0 * s)           # nearest of s, 3s (2s exact in fp64)
+    rec = np.where(np.signbit(b), -mag, mag)          # -0.0 counts as negative, like the sign bit
+    return rec.reshape(n, k).astype(np.float32)
+
+
+def layer_errors(w: np.ndarray, w_hat: np.ndarray, x_calib: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row reconstruction error of W_hat against W under the calibration
+    rows x_calib [N, k]: full e[r] = sum_i (sum_k d_rk x_ik)^2 and diagonal
+    e[r] = sum_k (sum_i x_ik^2) d_rk^2, d = W - W_hat, all in fp64."""
+    d = np.asarray(w, dtype=np.float64) - np.asarray(w_hat, dtype=np.float64)
+    x = np.asarray(x_calib, dtype=np.float64)
+    full = ((d @ x.T) ** 2).sum(axis=1)
+    diag = (d * d) @ (x * x).sum(axis=0)
+    return full, diag
+
+
+def greedy_allocation(gain: np.ndarray, extra_bytes: np.ndarray, budget: float) -> np.ndarray:
+    """Layers to move to the larger format: repeatedly take the layer with the
+    largest error reduction per added byte (lowest index on ties) while the
+    added bytes stay within `budget`; layers that no longer fit are skipped.
+    Returns a bool mask."""
+    gain = np.asarray(gain, dtype=np.float64)
+    extra = np.asarray(extra_bytes, dtype=np.float64)
+    order = sorted(range(len(gain)), key=lambda i: (-(gain[i] / extra[i]), i))
+    chosen = np.zeros(len(gain), dtype=bool)
+    used = 0.0
+    for i in order:
+        if gain[i] > 0 and used + extra[i] <= budget:
+            chosen[i] = True
+            used += extra[i]
+    return chosen
+
+
+def spearman(a: np.ndarray, b: np.ndarray) -> float:
+    """Spearman rank correlation (average ranks for ties)."""
+    def ranks(v):
+        v = np.asarray(v, dtype=np.float64)
+        order = np.argsort(v, kind="stable")
+        r = np.empty(len(v))
+        r[order] = np.arange(len(v), dtype=np.float64)
+        for val in np.unique(v):
+            m = v == val
+            if m.sum() > 1:
+                r[m] = r[m].mean()
+        return r
+    ra, rb = ranks(a), ranks(b)
+    ra -= ra.mean()
+    rb -= rb.mean()
+    return float((ra * rb).sum() / np.sqrt((ra * ra).sum() * (rb * rb).sum()))

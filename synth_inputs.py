@@ -83,6 +83,27 @@ def heavy_tailed_imatrix(seed: int, n_vec: int, k: int, frac: float = 0.02, scal
     return imatrix_from_calibration(rng.normal(0.0, 1.0, size=(n_vec, k)) * sigma)
 
 
+def paired_channel_layer(seed: int, n_rows: int, k: int, n_vec: int, sign: float, coupling: float,
+                         std: float = WEIGHT_STD):
+    """One synthetic layer whose Hessian has strong off-diagonal terms.
+
+    Within every 256-column block, column j+128 is paired with column j: its
+    calibration activation is `coupling` * x_j plus independent noise of the
+    remaining variance, and its weight is `sign` * w_j.  Paired columns sit
+    in different groups of four, so a sign-symmetric quantizer makes their
+    weight errors equal up to `sign`; the off-diagonal Hessian terms then
+    scale the expected error by about 1 + sign * coupling against the
+    diagonal-only estimate.  Returns (w fp32 [n_rows, k], x fp32 [n_vec, k])."""
+    if k % 256:
+        raise ValueError("k must be a multiple of 256")
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, 1.0, size=(n_vec, k // 256, 2, 128))
+    x[:, :, 1] = coupling * x[:, :, 0] + np.sqrt(max(0.0, 1.0 - coupling * coupling)) * x[:, :, 1]
+    w = rng.normal(0.0, std, size=(n_rows, k // 256, 2, 128))
+    w[:, :, 1] = sign * w[:, :, 0]
+    return w.reshape(n_rows, k).astype(np.float32), x.reshape(n_vec, k).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------
 # named workloads
 # ----------------------------------------------------------------------------
