@@ -13,7 +13,11 @@ One step is one pass of the hot path over one batch of synthetic input:
     batch 1, 16, 64, reported beside the headline as `moe_ffn_decode`;
   * the encoder as a layer-scale workload (`encode_layer`): both encoders on
     8 experts' fp32 gate/up weights drawn beforehand, extrapolated to the
-    256-expert layer.
+    256-expert layer;
+  * layer-sensitivity scoring (`layer_sensitivity`): full-Hessian and
+    diagonal error of one expert's STQ1_0 gate/up matrix (4096 x 7168) under
+    512 calibration rows, a dense fp64 contraction on the matrix cores, and
+    the 2-bit stand-in's quantize-and-reconstruct pass.
 Inputs are resident in HBM before timing starts.  `value` is the GEMV's
 effective bandwidth over the sweep: algorithmic bytes (each touched expert's
 packed bytes once, plus activations and outputs) divided by GEMV time.
@@ -42,6 +46,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP64_PEAK_TFLOPS = 78.6      # MI355X fp64 (matrix and vector)
+SENS_CALIB = 512             # calibration rows of the sensitivity workload
 BATCHES = (1, 4, 16, 64)
 FFN_BATCHES = (1, 16, 64)
 ENCODE_EXPERTS = 8
@@ -187,6 +193,8 @@ def main() -> int:
                     help="also time the batch-1 single-expert GEMV over 100 resident experts")
     ap.add_argument("--no-encode", action="store_true",
                     help="skip the timed layer-scale encode (8 experts, both encoders)")
+    ap.add_argument("--no-sensitivity", action="store_true",
+                    help="skip the layer-sensitivity scoring workload")
     ap.add_argument("--no-ffn", action="store_true",
                     help="skip the routed-expert FFN lines (profiling runs of the GEMV and GEMM alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -335,6 +343,51 @@ def main() -> int:
                              "fp32_read_GB/s": round(N * K * 4 / (ms * 1e-3) / 1e9, 1)}
         del ws, outq
 
+    sens_out = None
+    if not args.no_sensitivity:
+        # full-Hessian vs diagonal scoring of one expert's gate/up matrix: the
+        # weights, their STQ1_0 reconstruction and the calibration rows are
+        # resident before timing; only stq_layer_errors (and separately the
+        # 2-bit stand-in pass) is timed
+        w0 = S.torch_expert_weights(W.TABLE_SEED, 0, N, K, device=dev)
+        gx = torch.Generator(device=dev)
+        gx.manual_seed(4242)
+        xc = torch.randn((SENS_CALIB, K), generator=gx, device=dev, dtype=torch.float32)
+        xc.mul_(torch.rand((1, K), generator=gx, device=dev, dtype=torch.float32).mul_(9.9).add_(0.1))
+        w0_hat = stq.dequantize_rows(stq.quantize_rows(w0, (xc * xc).mean(dim=0)), N, K)
+        ef = torch.empty(N, dtype=torch.float64, device=dev)
+        ed = torch.empty(N, dtype=torch.float64, device=dev)
+        q2o = torch.empty_like(w0)
+        stq.layer_errors(w0, w0_hat, xc, ef, ed)  # warm (sizes the scratch arena)
+        stq.q2_roundtrip(w0, q2o)
+        reps = 5
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            stq.layer_errors(w0, w0_hat, xc, ef, ed)
+        b.record(stream)
+        c, d_ = ev(), ev()
+        c.record(stream)
+        for _ in range(reps):
+            stq.q2_roundtrip(w0, q2o)
+        d_.record(stream)
+        torch.cuda.synchronize()
+        le_ms = a.elapsed_time(b) / reps
+        q2_ms = c.elapsed_time(d_) / reps
+        flop = 2.0 * N * K * SENS_CALIB
+        tf = flop / (le_ms * 1e-3) / 1e12
+        sens_out = {"rows": N, "k": K, "calibration_rows": SENS_CALIB,
+                    "layer_errors_us": round(1e3 * le_ms, 1),
+                    "roofline": {"bound": "mfma", "dtype": "f64", "achieved": round(tf, 2),
+                                 "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(tf / FP64_PEAK_TFLOPS, 4),
+                                 "flop_per_call": flop,
+                                 "kernels": "hdiag_kernel + layer_errors_kernel + sum_partials_kernel"},
+                    "q2_roundtrip_us": round(1e3 * q2_ms, 1),
+                    "q2_roundtrip_GB/s": round(2 * N * K * 4 / (q2_ms * 1e-3) / 1e9, 1),
+                    "full_over_diag": round(float(ef.sum() / ed.sum()), 4)}
+        del w0, xc, w0_hat, ef, ed, q2o
+
     # ---------------- results ----------------
     gemv_ms = [a.elapsed_time(b) for (_, _, _, _, a, b) in rec["gemv"]]
     gemv_bytes = [nb for (_, _, nb, _, _, _) in rec["gemv"]]
@@ -396,6 +449,8 @@ def main() -> int:
         out["encode_layer"] = {"experts_timed": ENCODE_EXPERTS,
                                "weights_per_expert": N * K,
                                "rounds": 3, **enc_out}
+    if sens_out:
+        out["layer_sensitivity"] = sens_out
     if ffn:
         out["moe_ffn_decode"] = {"layer": "256 experts, top-8, gate/up 4096x7168 + down 7168x2048, STQ1_0",
                                  "bytes": "touched experts' packed gate/up and down matrices, x and y", **ffn}

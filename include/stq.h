@@ -41,8 +41,9 @@
  *     returns a status and stq_last_error() holds a message (thread-local);
  *   - STQ_E_HIP means a HIP call failed (launch, allocation); device faults
  *     surface at the caller's next synchronisation;
- *   - stq_gemv and stq_moe_ffn_decode share a per-device scratch arena that
- *     grows on demand with hipMalloc and is kept until the process ends;
+ *   - stq_gemv, stq_moe_ffn_decode and stq_layer_errors share a per-device
+ *     scratch arena that grows on demand with hipMalloc and is kept until the
+ *     process ends;
  *     calls that may overlap on one device must be issued on one stream from
  *     one host thread at a time.
  */
@@ -172,6 +173,54 @@ stq_status stq_grouped_gemm(const uint8_t* w_table, int64_t expert_stride_bytes,
                             int64_t n, int64_t k, const uint16_t* x_sorted,
                             const int32_t* expert_offsets, int64_t total_m, float* y,
                             stq_stream_t stream);
+
+/* Reconstruction error of an approximation W_hat of W under calibration
+ * activations, scored with the full Hessian H = X^T X and with its diagonal
+ * alone, the two layer-sensitivity measures the pages compare (lemmy post
+ * 66506, paragraph "Full-Hessian scoring": off-diagonal terms carry the
+ * input correlations that a diagonal-only imatrix misses).  With
+ * D = W - W_hat in fp64:
+ *     err_full[r] = sum_i (D_r . x_i)^2      = D_r H D_r^T
+ *     err_diag[r] = sum_c H_cc D_rc^2,        H_cc = sum_i x_ic^2
+ *   w, w_hat   [n_rows, k] fp32, row-major, 16-byte aligned (w_hat is
+ *              typically stq_dequantize_rows or stq_q2_roundtrip of w)
+ *   x_calib    [n_calib, k] fp32 calibration activations, row-major,
+ *              16-byte aligned; n_calib >= 1
+ *   err_full, err_diag   [n_rows] fp64, 8-byte aligned
+ * Products are exact (fp32 operands in fp64); D X^T accumulates in fp64 on
+ * the matrix cores, so the results agree with an fp64 reference to within
+ * the fp64 rounding of sums of k and n_calib terms.  The summation order is
+ * fixed: repeated calls give identical bits.  Non-finite inputs give
+ * non-finite outputs.  Scratch: 8*(k + 2*ceil(n_calib/64)*n_rows) bytes of
+ * the arena. */
+stq_status stq_layer_errors(const float* w, const float* w_hat, int64_t n_rows, int64_t k,
+                            const float* x_calib, int64_t n_calib, double* err_full, double* err_diag,
+                            stq_stream_t stream);
+
+/* Quantize-and-reconstruct through the plain 2-bit format this library uses
+ * as the larger partner format of a per-layer allocation (the pages pair
+ * STQ1_0 with IQ2_XXS at 2.0625 bits per weight, lemmy post 66506,
+ * paragraph "Precision follows weight sensitivity", without defining it; a
+ * stand-in of the same size takes its place: 66 bytes per 256 weights).
+ * Per 256-weight block: ss = sum of w^2 in fp64 (the four weights of a
+ * group in order, then a balanced tree of adjacent groups), s = fp16 of
+ * sqrt(ss/256)/2 (fp64 -> fp32 -> fp16, round-to-nearest-even, clamped to
+ * 65504); each weight becomes s if |w| < 2s, else 3s, with the sign bit of w.
+ *   w, out  [n_rows, k] fp32, row-major, 16-byte aligned (may not overlap)
+ * Bit-identical to the reference definition.  Non-finite inputs give
+ * unspecified (non-finite) outputs for their block. */
+stq_status stq_q2_roundtrip(const float* w, int64_t n_rows, int64_t k, float* out, stq_stream_t stream);
+
+/* Greedy per-byte allocation of the larger format over layers (lemmy post
+ * 66506, paragraph "Full-Hessian scoring": layers are taken greedily by
+ * error reduction per added byte).  Visit layers by gain/extra_bytes,
+ * largest first (lowest index on ties); take a layer when its gain is > 0
+ * and the added bytes still fit within `budget`, else skip it.
+ *   gain, extra_bytes   HOST double [n_layers]; extra_bytes > 0
+ *   chosen              HOST uint8 [n_layers], 1 for a layer taken
+ * Pure host function. */
+stq_status stq_greedy_allocation(const double* gain, const double* extra_bytes, int64_t n_layers,
+                                 double budget, uint8_t* chosen);
 
 /* Static text of a status code. */
 const char* stq_status_string(stq_status s);

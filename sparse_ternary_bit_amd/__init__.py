@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "QK", "BLOCK_BYTES", "ENC_WLS", "ENC_AMAX", "StqError", "lib", "lib_path",
-    "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "grouped_gemm",
+    "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "grouped_gemm", "moe_ffn_decode",
+    "layer_errors", "q2_roundtrip", "greedy_allocation",
 ]
 
 QK = 256
@@ -70,6 +71,12 @@ def lib() -> ctypes.CDLL:
     L.stq_moe_ffn_decode.argtypes = [_c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
                                      _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
     L.stq_moe_ffn_decode.restype = _c_int
+    L.stq_layer_errors.argtypes = [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp]
+    L.stq_layer_errors.restype = _c_int
+    L.stq_q2_roundtrip.argtypes = [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]
+    L.stq_q2_roundtrip.restype = _c_int
+    L.stq_greedy_allocation.argtypes = [_c_vp, _c_vp, _c_i64, ctypes.c_double, _c_vp]
+    L.stq_greedy_allocation.restype = _c_int
     _lib = L
     return L
 
@@ -211,3 +218,55 @@ def moe_ffn_decode(w_gate_up: torch.Tensor, gate_up_stride: int, w_down: torch.T
                                     pair_expert.data_ptr(), pair_weight.data_ptr(), int(top_k), out.data_ptr(),
                                     _stream()))
     return out
+
+
+def layer_errors(w: torch.Tensor, w_hat: torch.Tensor, x_calib: torch.Tensor,
+                 out_full: torch.Tensor | None = None, out_diag: torch.Tensor | None = None):
+    """Per-row error of w_hat against w under calibration rows x_calib fp32 [N, k]: full-Hessian
+    sum_i ((w - w_hat) . x_i)^2 and diagonal sum_c H_cc (w - w_hat)_c^2, both fp64 [n]."""
+    _on_gpu("w", w, torch.float32)
+    _on_gpu("w_hat", w_hat, torch.float32)
+    _on_gpu("x_calib", x_calib, torch.float32)
+    n, k = w.shape
+    if tuple(w_hat.shape) != (n, k) or x_calib.dim() != 2 or x_calib.shape[1] != k:
+        raise ValueError("w, w_hat must be [n, k] and x_calib [N, k]")
+    if out_full is None:
+        out_full = torch.empty(n, dtype=torch.float64, device=w.device)
+    if out_diag is None:
+        out_diag = torch.empty(n, dtype=torch.float64, device=w.device)
+    _on_gpu("out_full", out_full, torch.float64)
+    _on_gpu("out_diag", out_diag, torch.float64)
+    if out_full.numel() < n or out_diag.numel() < n:
+        raise ValueError("outputs must hold n entries")
+    _check("stq_layer_errors", lib().stq_layer_errors(w.data_ptr(), w_hat.data_ptr(), n, k, x_calib.data_ptr(),
+                                                      x_calib.shape[0], out_full.data_ptr(), out_diag.data_ptr(),
+                                                      _stream()))
+    return out_full, out_diag
+
+
+def q2_roundtrip(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Reconstruction of fp32 rows [n, k] through the 2-bit stand-in format (fp16 rms/2 scale per
+    256 weights, levels +-s, +-3s)."""
+    _on_gpu("w", w, torch.float32)
+    n, k = w.shape
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    _on_gpu("out", out, torch.float32)
+    if tuple(out.shape) != (n, k):
+        raise ValueError("out must be [n, k]")
+    _check("stq_q2_roundtrip", lib().stq_q2_roundtrip(w.data_ptr(), n, k, out.data_ptr(), _stream()))
+    return out
+
+
+def greedy_allocation(gain, extra_bytes, budget: float):
+    """Layers to move to the larger format, taken by error reduction per added byte within
+    `budget` bytes (host function; numpy in, numpy bool mask out)."""
+    import numpy as np
+    g = np.ascontiguousarray(gain, dtype=np.float64)
+    e = np.ascontiguousarray(extra_bytes, dtype=np.float64)
+    if g.shape != e.shape or g.ndim != 1:
+        raise ValueError("gain and extra_bytes must be 1-D of equal length")
+    chosen = np.zeros(g.shape[0], dtype=np.uint8)
+    _check("stq_greedy_allocation", lib().stq_greedy_allocation(g.ctypes.data, e.ctypes.data, g.shape[0],
+                                                                float(budget), chosen.ctypes.data))
+    return chosen.astype(bool)

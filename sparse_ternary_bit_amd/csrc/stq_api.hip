@@ -10,6 +10,7 @@
 #include <mutex>
 #include <string>
 #include <unordered_map>
+#include <vector>
 
 #include "stq.h"
 #include "stq_launch.hpp"
@@ -221,6 +222,65 @@ stq_status stq_grouped_gemm(const uint8_t* w_table, int64_t expert_stride_bytes,
   stq::GemmArgs ga{w_table, expert_stride_bytes, n_experts, n, k, x_sorted, expert_offsets, total_m, y};
   hipError_t e = stq::launch_grouped_gemm(ga, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "stq_grouped_gemm launch");
+  return ok();
+}
+
+stq_status stq_layer_errors(const float* w, const float* w_hat, int64_t n_rows, int64_t k, const float* x_calib,
+                            int64_t n_calib, double* err_full, double* err_diag, stq_stream_t stream) {
+  if (n_rows < 0) return fail(STQ_E_ARG, "stq_layer_errors: n_rows < 0");
+  if (n_calib < 1) return fail(STQ_E_ARG, "stq_layer_errors: n_calib must be >= 1");
+  if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "stq_layer_errors: k=%lld is not a positive multiple of 256", (long long)k);
+  if (n_rows > INT_MAX || n_calib > INT_MAX) return fail(STQ_E_SHAPE, "stq_layer_errors: count exceeds int32");
+  if ((n_calib + 63) / 64 > 65535) return fail(STQ_E_SHAPE, "stq_layer_errors: more than 65535*64 calibration rows");
+  if (n_rows == 0) return ok();
+  if (!w || !w_hat || !x_calib || !err_full || !err_diag) return fail(STQ_E_ARG, "stq_layer_errors: null pointer");
+  if (!aligned(w, 16) || !aligned(w_hat, 16) || !aligned(x_calib, 16))
+    return fail(STQ_E_ALIGN, "stq_layer_errors: w, w_hat and x_calib must be 16-byte aligned");
+  if (!aligned(err_full, 8) || !aligned(err_diag, 8)) return fail(STQ_E_ALIGN, "stq_layer_errors: outputs not 8-byte aligned");
+  void* scratch = nullptr;
+  const stq_status st = arena_get(stq::layer_errors_scratch_bytes(n_rows, k, n_calib), &scratch, "stq_layer_errors: scratch");
+  if (st != STQ_OK) return st;
+  hipError_t e = stq::launch_layer_errors(w, w_hat, n_rows, k, x_calib, n_calib, err_full, err_diag, scratch,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stq_layer_errors launch");
+  return ok();
+}
+
+stq_status stq_q2_roundtrip(const float* w, int64_t n_rows, int64_t k, float* out, stq_stream_t stream) {
+  if (n_rows < 0) return fail(STQ_E_ARG, "stq_q2_roundtrip: n_rows < 0");
+  if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "stq_q2_roundtrip: k=%lld is not a positive multiple of 256", (long long)k);
+  if (n_rows > INT_MAX || n_rows * (k / STQ_QK) > (int64_t)INT_MAX * 4) return fail(STQ_E_SHAPE, "stq_q2_roundtrip: too many blocks");
+  if (n_rows == 0) return ok();
+  if (!w || !out) return fail(STQ_E_ARG, "stq_q2_roundtrip: null pointer");
+  if (!aligned(w, 16) || !aligned(out, 16)) return fail(STQ_E_ALIGN, "stq_q2_roundtrip: w and out must be 16-byte aligned");
+  hipError_t e = stq::launch_q2_roundtrip(w, n_rows, k, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stq_q2_roundtrip launch");
+  return ok();
+}
+
+stq_status stq_greedy_allocation(const double* gain, const double* extra_bytes, int64_t n_layers, double budget,
+                                 uint8_t* chosen) {
+  if (n_layers < 0) return fail(STQ_E_ARG, "stq_greedy_allocation: n_layers < 0");
+  if (n_layers == 0) return ok();
+  if (!gain || !extra_bytes || !chosen) return fail(STQ_E_ARG, "stq_greedy_allocation: null pointer");
+  for (int64_t i = 0; i < n_layers; ++i)
+    if (!(extra_bytes[i] > 0.0)) return fail(STQ_E_ARG, "stq_greedy_allocation: extra_bytes[%lld] must be > 0", (long long)i);
+  std::vector<int64_t> order(static_cast<size_t>(n_layers));
+  std::vector<double> ratio(static_cast<size_t>(n_layers));
+  for (int64_t i = 0; i < n_layers; ++i) {
+    order[i] = i;
+    ratio[i] = gain[i] / extra_bytes[i];
+  }
+  // largest reduction per added byte first, lowest index on ties
+  std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) { return ratio[a] > ratio[b]; });
+  double used = 0.0;
+  for (int64_t i = 0; i < n_layers; ++i) chosen[i] = 0;
+  for (int64_t i : order) {
+    if (gain[i] > 0.0 && used + extra_bytes[i] <= budget) {
+      chosen[i] = 1;
+      used += extra_bytes[i];
+    }
+  }
   return ok();
 }
 

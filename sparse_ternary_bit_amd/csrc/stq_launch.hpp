@@ -57,4 +57,13 @@ struct GemmArgs {
 };
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t s);
 
+// Layer error under calibration activations (full Hessian and diagonal);
+// `scratch` holds layer_errors_scratch_bytes(...) bytes.
+int64_t layer_errors_scratch_bytes(int64_t n_rows, int64_t k, int64_t n_cal);
+hipError_t launch_layer_errors(const float* w, const float* w_hat, int64_t n_rows, int64_t k, const float* x,
+                               int64_t n_cal, double* err_full, double* err_diag, void* scratch, hipStream_t s);
+
+// 2-bit stand-in format: quantize and reconstruct in one pass
+hipError_t launch_q2_roundtrip(const float* w, int64_t n_rows, int64_t k, float* out, hipStream_t s);
+
 }  // namespace stq

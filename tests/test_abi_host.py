@@ -22,13 +22,14 @@ def L():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(stq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(stq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for want in ("stq_quantize_rows", "stq_gemv", "stq_grouped_gemm", "stq_dequantize_rows",
-                 "stq_moe_ffn_decode", "stq_row_bytes", "stq_status_string", "stq_last_error"):
+                 "stq_moe_ffn_decode", "stq_layer_errors", "stq_q2_roundtrip", "stq_greedy_allocation",
+                 "stq_row_bytes", "stq_status_string", "stq_last_error"):
         assert want in names
 
 
@@ -145,3 +146,56 @@ def test_moe_ffn_rejects_bad_arguments(L):
     assert f(gs=gu_stride + 8) == 3
     assert f(x=FAKE + 2) == 3
     assert f(t=0, wg=None, wd=None, x=None, pe=None, pw=None, y=None) == 0
+
+
+def test_layer_errors_rejects_bad_arguments(L):
+    le = L.stq_layer_errors
+    assert le(FAKE, FAKE, 4, 300, FAKE, 8, FAKE, FAKE, None) == 2
+    assert le(FAKE, FAKE, 4, 256, FAKE, 0, FAKE, FAKE, None) == 1
+    assert "n_calib" in _err(L)
+    assert le(FAKE, FAKE, -1, 256, FAKE, 8, FAKE, FAKE, None) == 1
+    assert le(FAKE, None, 4, 256, FAKE, 8, FAKE, FAKE, None) == 1
+    assert le(FAKE + 4, FAKE, 4, 256, FAKE, 8, FAKE, FAKE, None) == 3
+    assert le(FAKE, FAKE, 4, 256, FAKE + 8, 8, FAKE, FAKE, None) == 3
+    assert le(FAKE, FAKE, 4, 256, FAKE, 8, FAKE + 4, FAKE, None) == 3
+    assert le(FAKE, FAKE, 4, 256, FAKE, 65536 * 64, FAKE, FAKE, None) == 2
+    assert le(None, None, 0, 256, None, 8, None, None, None) == 0   # nothing to do
+
+
+def test_q2_roundtrip_rejects_bad_arguments(L):
+    q2 = L.stq_q2_roundtrip
+    assert q2(FAKE, 4, 128, FAKE, None) == 2
+    assert q2(FAKE, -2, 256, FAKE, None) == 1
+    assert q2(None, 4, 256, FAKE, None) == 1
+    assert q2(FAKE + 4, 4, 256, FAKE, None) == 3
+    assert q2(FAKE, 4, 256, FAKE + 8, None) == 3
+    assert q2(None, 0, 256, None, None) == 0
+
+
+def test_greedy_allocation_rejects_bad_arguments(L):
+    import numpy as np
+    g = np.ones(3)
+    e = np.array([1.0, 0.0, 2.0])
+    c = np.zeros(3, dtype=np.uint8)
+    assert L.stq_greedy_allocation(g.ctypes.data, e.ctypes.data, 3, 10.0, c.ctypes.data) == 1
+    assert "extra_bytes[1]" in _err(L)
+    assert L.stq_greedy_allocation(None, e.ctypes.data, 3, 10.0, c.ctypes.data) == 1
+    assert L.stq_greedy_allocation(g.ctypes.data, e.ctypes.data, -1, 10.0, c.ctypes.data) == 1
+
+
+def test_greedy_allocation_matches_the_oracle(L):
+    """A host function: its choice equals the oracle's on random layer sets,
+    ties in the ratio included."""
+    import numpy as np
+    import sparse_ternary_bit_amd as stq
+    from oracle import stq_oracle as O
+    rng = np.random.default_rng(0)
+    for trial in range(200):
+        n = int(rng.integers(1, 40))
+        gain = rng.normal(1.0, 1.0, n)
+        gain[rng.random(n) < 0.2] = 2.0          # equal gains with equal sizes: ties
+        extra = rng.choice([1.0, 2.0, 3.0], n)
+        budget = float(rng.uniform(0, extra.sum()))
+        got = stq.greedy_allocation(gain, extra, budget)
+        want = O.greedy_allocation(gain, extra, budget)
+        assert np.array_equal(got, want), trial
