@@ -35,7 +35,10 @@ reduction order, rounding of d, the starting pattern); each is stated at the
 function that makes it.
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
-against enumeration, exact rational arithmetic, closed forms or brute force.
+(format, encoder, GEMV), ``tests/test_oracle_ffn.py`` (routed-expert FFN) and
+``tests/test_oracle_sensitivity.py`` (layer error, the 2-bit stand-in,
+greedy allocation) against enumeration, exact rational arithmetic, closed
+forms, hand-built cases or brute force.
 """
 from __future__ import annotations
 
@@ -565,6 +568,33 @@ def layer_errors(w: np.ndarray, w_hat: np.ndarray, x_calib: np.ndarray) -> tuple
     full = ((d @ x.T) ** 2).sum(axis=1)
     diag = (d * d) @ (x * x).sum(axis=0)
     return full, diag
+
+
+def layer_errors_tolerance(w: np.ndarray, w_hat: np.ndarray, x_calib: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row bounds on |err - err_ref| for two fp64 evaluations of
+    layer_errors that differ only in summation order (the pages fix no
+    precision; this is the standard fp64 bound, u = 2^-53, g(m) = m u/(1-m u)).
+
+    Each p_ri = D_r . x_i sums k products, one rounding each for the
+    difference, the product and every addition, so two evaluations differ by
+    at most delta_ri = 2 g(k+2) A_ri with A_ri = sum_c |D_rc x_ic|; squaring
+    moves p^2 by at most delta (2|p| + delta); the N nonnegative squares add
+    with relative error g(N+1) on either side.  The diagonal sum has only
+    nonnegative terms of k + N + 4 roundings each side."""
+    d = np.asarray(w, dtype=np.float64) - np.asarray(w_hat, dtype=np.float64)
+    x = np.asarray(x_calib, dtype=np.float64)
+    u = 2.0 ** -53
+    g = lambda m: m * u / (1.0 - m * u)
+    k, n_cal = d.shape[1], x.shape[0]
+    p = d @ x.T
+    a = np.abs(d) @ np.abs(x).T
+    delta = 2.0 * g(k + 2) * a
+    sq = (delta * (2.0 * np.abs(p) + delta)).sum(axis=1)
+    full = (p * p).sum(axis=1)
+    b_full = sq + 2.0 * g(n_cal + 1) * (full + sq)
+    diag = (d * d) @ (x * x).sum(axis=0)
+    b_diag = 2.0 * g(k + n_cal + 4) * diag
+    return b_full, b_diag
 
 
 def greedy_allocation(gain: np.ndarray, extra_bytes: np.ndarray, budget: float) -> np.ndarray:

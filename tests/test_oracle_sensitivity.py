@@ -32,6 +32,28 @@ def test_full_error_by_brute_force():
         assert abs(full[r] - f) <= 1e-12 * f and abs(diag[r] - d) <= 1e-12 * d
 
 
+def test_tolerance_covers_an_exactly_rounded_evaluation():
+    """math.fsum gives each dot product and each final sum correctly rounded;
+    the oracle's numpy evaluation stays within the stated bound of it, and
+    the bound is tiny against the errors themselves."""
+    import math
+    rng = np.random.default_rng(2)
+    w = rng.normal(0, 0.02, (6, 512)).astype(np.float32)
+    w_hat = O.q2_roundtrip(w)
+    x = (rng.normal(0, 1, (40, 512)) * rng.uniform(0.1, 10, 512)).astype(np.float32)
+    full, diag = O.layer_errors(w, w_hat, x)
+    b_full, b_diag = O.layer_errors_tolerance(w, w_hat, x)
+    d = w.astype(np.float64) - w_hat.astype(np.float64)
+    xd = x.astype(np.float64)
+    hd = [math.fsum(xd[:, c] ** 2) for c in range(512)]
+    for r in range(6):
+        p = [math.fsum(d[r] * xd[i]) for i in range(40)]
+        f = math.fsum(v * v for v in p)
+        g = math.fsum(hd[c] * d[r, c] ** 2 for c in range(512))
+        assert abs(full[r] - f) <= b_full[r] and abs(diag[r] - g) <= b_diag[r]
+    assert np.all(b_full < 1e-9 * full) and np.all(b_diag < 1e-12 * diag)
+
+
 def test_q2_hand_block():
     # 192 weights of 0.6 and 64 of -1.8: mean square 1.08, rms 1.0392..., s = rms/2 -> fp16 0.51953125;
     # 0.6 < 2s = 1.0390625 takes s, 1.8 takes 3s
