@@ -63,6 +63,11 @@ __device__ __forceinline__ void stage_store(double* dp, float* xp, float4 wv, fl
   }
 }
 
+// one chunk's global loads of one thread: two float4 slots of w, w_hat and x
+struct Stage {
+  float4 w0, w1, h0, h1, x0, x1;
+};
+
 struct SensSmem {
   double d[2][kSensRows][kDPitch];
   float x[2][kSensCal][kXPitch];
@@ -77,15 +82,24 @@ __global__ __launch_bounds__(256) void layer_errors_kernel(const float* __restri
                                                            const float* __restrict__ x, int n_cal,
                                                            const double* __restrict__ hd,
                                                            double* __restrict__ partial,
-                                                           double* __restrict__ err_diag) {
+                                                           double* __restrict__ err_diag, int ctiles) {
   __shared__ SensSmem sm;
+  // workgroup -> (row tile, calibration tile): ids are dealt to the 8 XCDs
+  // round robin, so id = 8 * (ctiles * g + ct) + x holds row tile 8g + x
+  // with every calibration tile on XCD x, dispatched together; they stream
+  // the same weight rows through that XCD's L2
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  const int ct = local % ctiles;
+  const int rt = (local / ctiles) * 8 + xcd;
+  const int r0 = rt * kSensRows;
+  if (r0 >= n_rows) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const int r0 = blockIdx.x * kSensRows;
-  const int c0 = blockIdx.y * kSensCal;
-  const bool with_diag = blockIdx.y == 0;
+  const int c0 = ct * kSensCal;
+  const bool with_diag = ct == 0;
   const int n_chunks = static_cast<int>(k / kSensK);
 
   // staging: thread t moves float4 slots t and t + 256 of each 64 x 32 tile
@@ -101,25 +115,26 @@ __global__ __launch_bounds__(256) void layer_errors_kernel(const float* __restri
   const float* hp1 = w_hat + static_cast<int64_t>(min(r0 + srow1, n_rows - 1)) * k + 4 * c4;
   const float* xp0 = x + static_cast<int64_t>(min(c0 + srow0, n_cal - 1)) * k + 4 * c4;
   const float* xp1 = x + static_cast<int64_t>(min(c0 + srow1, n_cal - 1)) * k + 4 * c4;
-  float4 wv0, wv1, hv0, hv1, xv0, xv1;
   double dacc0 = 0.0, dacc1 = 0.0;
 
-#define STQ_SENS_LOAD(ch)                                                  \
-  do {                                                                     \
-    const int64_t kc_ = static_cast<int64_t>(ch) * kSensK;                 \
-    wv0 = *reinterpret_cast<const float4*>(wp0 + kc_);                     \
-    wv1 = *reinterpret_cast<const float4*>(wp1 + kc_);                     \
-    hv0 = *reinterpret_cast<const float4*>(hp0 + kc_);                     \
-    hv1 = *reinterpret_cast<const float4*>(hp1 + kc_);                     \
-    xv0 = *reinterpret_cast<const float4*>(xp0 + kc_);                     \
-    xv1 = *reinterpret_cast<const float4*>(xp1 + kc_);                     \
-  } while (0)
-
-  STQ_SENS_LOAD(0);
-  stage_store(sm.d[0][srow0] + 4 * c4, sm.x[0][srow0] + 4 * c4, wv0, hv0, xv0, wok0, xok0, with_diag, hd + 4 * c4,
-              dacc0);
-  stage_store(sm.d[0][srow1] + 4 * c4, sm.x[0][srow1] + 4 * c4, wv1, hv1, xv1, wok1, xok1, with_diag, hd + 4 * c4,
-              dacc1);
+  // Global loads run two chunks ahead (two register sets, used alternately),
+  // so a chunk's weights have two chunks' MFMA time to arrive.
+  auto load = [&](Stage& st, int ch) {
+    const int64_t kc = static_cast<int64_t>(ch) * kSensK;
+    st.w0 = *reinterpret_cast<const float4*>(wp0 + kc);
+    st.w1 = *reinterpret_cast<const float4*>(wp1 + kc);
+    st.h0 = *reinterpret_cast<const float4*>(hp0 + kc);
+    st.h1 = *reinterpret_cast<const float4*>(hp1 + kc);
+    st.x0 = *reinterpret_cast<const float4*>(xp0 + kc);
+    st.x1 = *reinterpret_cast<const float4*>(xp1 + kc);
+  };
+  auto store = [&](const Stage& st, int ch, int buf) {
+    const double* h = hd + static_cast<int64_t>(ch) * kSensK + 4 * c4;
+    stage_store(sm.d[buf][srow0] + 4 * c4, sm.x[buf][srow0] + 4 * c4, st.w0, st.h0, st.x0, wok0, xok0, with_diag, h,
+                dacc0);
+    stage_store(sm.d[buf][srow1] + 4 * c4, sm.x[buf][srow1] + 4 * c4, st.w1, st.h1, st.x1, wok1, xok1, with_diag, h,
+                dacc1);
+  };
 
   double4_t acc[2][2];
 #pragma unroll
@@ -128,10 +143,7 @@ __global__ __launch_bounds__(256) void layer_errors_kernel(const float* __restri
     for (int b = 0; b < 2; ++b) acc[a][b] = double4_t{0.0, 0.0, 0.0, 0.0};
 
   const int li = lane & 15, lg = lane >> 4;
-  __syncthreads();
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const int buf = ch & 1;
-    if (ch + 1 < n_chunks) STQ_SENS_LOAD(ch + 1);
+  auto compute = [&](int buf) {
     double av[2][8];
     float bv[2][8];
 #pragma unroll
@@ -155,17 +167,25 @@ __global__ __launch_bounds__(256) void layer_errors_kernel(const float* __restri
       acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[1][s], b0, acc[1][0], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[1][s], b1, acc[1][1], 0, 0, 0);
     }
-    if (ch + 1 < n_chunks) {
-      // the other buffer was last read before the previous barrier
-      const int64_t kn = static_cast<int64_t>(ch + 1) * kSensK;
-      stage_store(sm.d[buf ^ 1][srow0] + 4 * c4, sm.x[buf ^ 1][srow0] + 4 * c4, wv0, hv0, xv0, wok0, xok0,
-                  with_diag, hd + kn + 4 * c4, dacc0);
-      stage_store(sm.d[buf ^ 1][srow1] + 4 * c4, sm.x[buf ^ 1][srow1] + 4 * c4, wv1, hv1, xv1, wok1, xok1,
-                  with_diag, hd + kn + 4 * c4, dacc1);
-    }
+  };
+
+  Stage sa, sb;
+  load(sa, 0);
+  if (n_chunks > 1) load(sb, 1);
+  store(sa, 0, 0);
+  __syncthreads();
+  // chunk ch computes from LDS buffer ch & 1; set A holds even chunks, set B odd ones
+  for (int ch = 0; ch < n_chunks; ch += 2) {
+    if (ch + 2 < n_chunks) load(sa, ch + 2);
+    compute(0);
+    if (ch + 1 < n_chunks) store(sb, ch + 1, 1);  // buffer 1 was last read before the previous barrier
+    __syncthreads();
+    if (ch + 1 >= n_chunks) break;
+    if (ch + 3 < n_chunks) load(sb, ch + 3);
+    compute(1);
+    if (ch + 2 < n_chunks) store(sa, ch + 2, 0);
     __syncthreads();
   }
-#undef STQ_SENS_LOAD
 
   // P tile (a, b): the fp64 16x16x4 result keeps row 4 * j + lg of the tile
   // in element j (j = 0..3) of lane 16 * lg + li, column li.  Sum the
@@ -181,7 +201,7 @@ __global__ __launch_bounds__(256) void layer_errors_kernel(const float* __restri
       for (int m = 1; m < 16; m <<= 1) s += __shfl_xor(s, m, 64);
       const int gr = r0 + 32 * wr + 16 * a + 4 * j + lg;
       if (li == 0 && gr < n_rows)
-        partial[(static_cast<int64_t>(blockIdx.y) * 2 + wc) * n_rows + gr] = s;
+        partial[(static_cast<int64_t>(ct) * 2 + wc) * n_rows + gr] = s;
     }
   }
   if (with_diag) {
@@ -260,8 +280,9 @@ hipError_t launch_layer_errors(const float* w, const float* w_hat, int64_t n_row
   const int rtiles = static_cast<int>((n_rows + kSensRows - 1) / kSensRows);
   const int ctiles = static_cast<int>(cal_tiles(n_cal));
   hipLaunchKernelGGL(hdiag_kernel, dim3(static_cast<unsigned>((k + 255) / 256)), dim3(256), 0, s, x, n_cal, k, hd);
-  hipLaunchKernelGGL(layer_errors_kernel, dim3(rtiles, ctiles), dim3(256), 0, s, w, w_hat,
-                     static_cast<int>(n_rows), k, x, static_cast<int>(n_cal), hd, partial, err_diag);
+  const int64_t groups = (rtiles + 7) / 8;
+  hipLaunchKernelGGL(layer_errors_kernel, dim3(static_cast<unsigned>(groups * 8 * ctiles)), dim3(256), 0, s, w,
+                     w_hat, static_cast<int>(n_rows), k, x, static_cast<int>(n_cal), hd, partial, err_diag, ctiles);
   hipLaunchKernelGGL(sum_partials_kernel, dim3(static_cast<unsigned>((n_rows + 255) / 256)), dim3(256), 0, s,
                      partial, 2 * ctiles, static_cast<int>(n_rows), err_full);
   return hipGetLastError();

@@ -232,6 +232,7 @@ stq_status stq_layer_errors(const float* w, const float* w_hat, int64_t n_rows, 
   if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "stq_layer_errors: k=%lld is not a positive multiple of 256", (long long)k);
   if (n_rows > INT_MAX || n_calib > INT_MAX) return fail(STQ_E_SHAPE, "stq_layer_errors: count exceeds int32");
   if ((n_calib + 63) / 64 > 65535) return fail(STQ_E_SHAPE, "stq_layer_errors: more than 65535*64 calibration rows");
+  if (((n_rows + 511) / 512) * 8 * ((n_calib + 63) / 64) > INT_MAX) return fail(STQ_E_SHAPE, "stq_layer_errors: too many tiles");
   if (n_rows == 0) return ok();
   if (!w || !w_hat || !x_calib || !err_full || !err_diag) return fail(STQ_E_ARG, "stq_layer_errors: null pointer");
   if (!aligned(w, 16) || !aligned(w_hat, 16) || !aligned(x_calib, 16))
