@@ -222,6 +222,14 @@ stq_status stq_q2_roundtrip(const float* w, int64_t n_rows, int64_t k, float* ou
 stq_status stq_greedy_allocation(const double* gain, const double* extra_bytes, int64_t n_layers,
                                  double budget, uint8_t* chosen);
 
+/* Measurement helper, not part of the method: reads `bytes` bytes of the
+ * device buffer `buf` once with 16-byte loads, the streaming-read rate this
+ * GPU sustains, against which the decode GEMV's effective bandwidth is
+ * compared (the HBM roofline).  `buf` 16-byte aligned, `bytes` a multiple of
+ * 16; `sink` is one device uint32 that may be overwritten (its value is
+ * meaningless). */
+stq_status stq_stream_read_probe(const void* buf, int64_t bytes, uint32_t* sink, stq_stream_t stream);
+
 /* Static text of a status code. */
 const char* stq_status_string(stq_status s);
 

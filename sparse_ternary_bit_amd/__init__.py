@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "QK", "BLOCK_BYTES", "ENC_WLS", "ENC_AMAX", "StqError", "lib", "lib_path",
     "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "grouped_gemm", "moe_ffn_decode",
-    "layer_errors", "q2_roundtrip", "greedy_allocation",
+    "layer_errors", "q2_roundtrip", "greedy_allocation", "stream_read_probe",
 ]
 
 QK = 256
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.stq_q2_roundtrip.restype = _c_int
     L.stq_greedy_allocation.argtypes = [_c_vp, _c_vp, _c_i64, ctypes.c_double, _c_vp]
     L.stq_greedy_allocation.restype = _c_int
+    L.stq_stream_read_probe.argtypes = [_c_vp, _c_i64, _c_vp, _c_vp]
+    L.stq_stream_read_probe.restype = _c_int
     _lib = L
     return L
 
@@ -270,3 +272,14 @@ def greedy_allocation(gain, extra_bytes, budget: float):
     _check("stq_greedy_allocation", lib().stq_greedy_allocation(g.ctypes.data, e.ctypes.data, g.shape[0],
                                                                 float(budget), chosen.ctypes.data))
     return chosen.astype(bool)
+
+
+def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of the GPU tensor `buf` once (a streaming-read rate
+    reference for the HBM roofline); `sink` is a one-element int32 GPU tensor."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _on_gpu("sink", sink, torch.int32)
+    nbytes = buf.numel() * buf.element_size()
+    _check("stq_stream_read_probe", lib().stq_stream_read_probe(buf.data_ptr(), nbytes - nbytes % 16,
+                                                                sink.data_ptr(), _stream()))

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstq.so")
 
-SOURCES = ["stq_api.hip", "k_codec.hip", "k_gemv.hip", "k_gemm.hip", "k_moe.hip", "k_sens.hip"]
+SOURCES = ["stq_api.hip", "k_codec.hip", "k_gemv.hip", "k_gemm.hip", "k_moe.hip", "k_sens.hip", "k_probe.hip"]
 # per-file extra flags: the encoders must not contract fp64 arithmetic
 EXTRA = {"k_codec.hip": ["-ffp-contract=off"], "k_sens.hip": ["-ffp-contract=off"]}
 

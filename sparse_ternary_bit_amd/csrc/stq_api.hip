@@ -285,4 +285,14 @@ stq_status stq_greedy_allocation(const double* gain, const double* extra_bytes, 
   return ok();
 }
 
+stq_status stq_stream_read_probe(const void* buf, int64_t bytes, uint32_t* sink, stq_stream_t stream) {
+  if (bytes < 0 || bytes % 16) return fail(STQ_E_ARG, "stq_stream_read_probe: bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return ok();
+  if (!buf || !sink) return fail(STQ_E_ARG, "stq_stream_read_probe: null pointer");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(STQ_E_ALIGN, "stq_stream_read_probe: buf must be 16-byte and sink 4-byte aligned");
+  hipError_t e = stq::launch_stream_read(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stq_stream_read_probe launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -66,4 +66,7 @@ hipError_t launch_layer_errors(const float* w, const float* w_hat, int64_t n_row
 // 2-bit stand-in format: quantize and reconstruct in one pass
 hipError_t launch_q2_roundtrip(const float* w, int64_t n_rows, int64_t k, float* out, hipStream_t s);
 
+// Streaming-read reference (measurement only): reads `bytes` bytes of `buf`
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
+
 }  // namespace stq

@@ -199,3 +199,11 @@ def test_greedy_allocation_matches_the_oracle(L):
         got = stq.greedy_allocation(gain, extra, budget)
         want = O.greedy_allocation(gain, extra, budget)
         assert np.array_equal(got, want), trial
+
+
+def test_stream_read_probe_rejects_bad_arguments(L):
+    assert L.stq_stream_read_probe(FAKE, 100, FAKE, None) == 1
+    assert L.stq_stream_read_probe(FAKE, -16, FAKE, None) == 1
+    assert L.stq_stream_read_probe(None, 64, FAKE, None) == 1
+    assert L.stq_stream_read_probe(FAKE + 8, 64, FAKE, None) == 3
+    assert L.stq_stream_read_probe(None, 0, None, None) == 0

@@ -312,3 +312,15 @@ def test_grouped_gemm_empty_and_single_rows(stq):
     gv = host(stq.gemv(dev(raw), raw.nbytes, 1, n, k, dev(xf[:1])))[0]
     A = O.tolerance_scale(raw, n, k, xf[0])[0]
     assert np.all(np.abs(gv - y[0]) <= 2 * GEMM_TOL * A)
+
+
+def test_stream_read_probe_runs(stq):
+    """The read-rate reference kernel (measurement only) over a small and a
+    ragged buffer: it completes and leaves the buffer untouched."""
+    buf = torch.arange(1 << 18, dtype=torch.int32, device="cuda")
+    before = buf.clone()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stq.stream_read_probe(buf, sink)
+    stq.stream_read_probe(buf[: 1000], sink)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
