@@ -29,13 +29,15 @@
 // gaps and never leave it) and realigns them with byte permutes.  Loads run
 // two blocks ahead, in the order they are consumed.
 //
-// k split: when few experts are active the blocks of a row are split over
-// several workgroups; each writes fp32 partial sums to scratch and a second
-// small kernel adds them in split order, so the result does not depend on
-// scheduling.
+// k split: the blocks of a row may be split over several workgroups (chosen
+// per call from the expected number of active experts, see plan_gemv); each
+// writes fp32 partial sums to scratch and a second small kernel adds them in
+// split order, so the result does not depend on scheduling.
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cmath>
 
 #include "stq_device.hpp"
 #include "stq_launch.hpp"
@@ -378,18 +380,52 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 
 }  // namespace
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// k split: the kernel keeps two workgroups resident per CU (its LDS tables),
+// so workgroups run in rounds of 2 * CUs.  The number of leading workgroups
+// is estimated from the pairs, assuming they spread over the experts
+// (expected distinct experts of n_pairs uniform draws).  Of the split counts,
+// take the one with the least rounds x (blocks per workgroup + ~2 blocks of
+// fixed cost: launch, pair scan, table and pipeline fill); ties go to fewer
+// splits.
 GemvPlan plan_gemv(const GemvArgs& a) {
   GemvPlan pl{};
   const int nb = static_cast<int>(a.k / kQK);
-  const int ntiles = static_cast<int>((a.n + kRows - 1) / kRows);
-  const int64_t active = std::min<int64_t>(a.n_pairs, a.n_experts);
-  const int64_t base_wgs = std::max<int64_t>(1, active * ntiles);
-  int64_t want = (512 + base_wgs - 1) / base_wgs;  // aim for >= ~2 workgroups per CU
-  if (want > nb) want = nb;
-  if (want < 1) want = 1;
-  const int bps = static_cast<int>((nb + want - 1) / want);
-  pl.blocks_per_split = bps;
-  pl.splits = (nb + bps - 1) / bps;
+  const int64_t ntiles = (a.n + kRows - 1) / kRows;
+  const double ne = static_cast<double>(a.n_experts);
+  const double distinct = std::min(static_cast<double>(a.n_pairs),
+                                   ne * (1.0 - std::pow(1.0 - 1.0 / ne, static_cast<double>(a.n_pairs))));
+  const double base_wgs = std::max(1.0, std::ceil(distinct) * static_cast<double>(ntiles));
+  const double slots = 2.0 * device_cus();
+  int best_splits = 1, best_bps = nb;
+  double best_cost = 0.0;
+  for (int splits = 1; splits <= nb; ++splits) {
+    const int bps = (nb + splits - 1) / splits;
+    if ((nb + bps - 1) / bps != splits) continue;  // the same split under another count
+    const double rounds = std::ceil(base_wgs * splits / slots);
+    const double cost = rounds * (bps + 2.0);
+    if (splits == 1 || cost < best_cost) {
+      best_cost = cost;
+      best_splits = splits;
+      best_bps = bps;
+    }
+  }
+  pl.blocks_per_split = best_bps;
+  pl.splits = best_splits;
   if (pl.splits > 1) pl.partial_bytes = static_cast<int64_t>(pl.splits) * a.n_pairs * a.n * 4;
   return pl;
 }
