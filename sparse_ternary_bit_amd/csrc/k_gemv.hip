@@ -81,6 +81,7 @@ struct Shared {
   int toks[kMT];
   int mc;
   int next;
+  int lead;
   int flag;
   unsigned long long ball[kWaves];
 };
@@ -288,31 +289,96 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   }
 }
 
+// A pair leads when its token is valid and no earlier valid pair names the
+// same expert; the leading pair of an expert collects all of that expert's
+// pairs (gather above).  Workgroup z serves the z-th leading pair in pair
+// order, so the workgroups with work are the first ones launched whatever
+// the order of the pairs: workgroups are dealt to the shader engines of an
+// XCD round robin, and a periodic pattern of idle workgroups (pairs sorted by
+// expert, say, with four pairs per expert) would otherwise put all the work
+// on one of them.
+constexpr int kLeadExperts = static_cast<int>(sizeof(Shared::tab) / sizeof(int));
+
+__device__ __forceinline__ bool pair_valid(const KArgs& a, int q, int& e) {
+  e = pair_expert(a, q);
+  const int t = pair_token(a, q);
+  return e >= 0 && e < a.n_experts && t >= 0 && t < a.n_tokens;
+}
+
+// With at most kLeadExperts experts: the first valid pair of every expert by
+// an LDS atomic minimum (in the table space, unused until the tables are
+// built), then a running count of leading pairs in pair order until the z-th.
+__device__ int find_leader(const KArgs& a, Shared& sh, int z) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int* first = reinterpret_cast<int*>(&sh.tab[0][0]);
+  for (int e = tid; e < a.n_experts; e += kRows) first[e] = 0x7FFFFFFF;
+  if (tid == 0) sh.lead = -1;
+  __syncthreads();
+  for (int q = tid; q < a.n_pairs; q += kRows) {
+    int e;
+    if (pair_valid(a, q, e)) atomicMin(&first[e], q);
+  }
+  __syncthreads();
+  int base = 0;
+  for (int c = 0; c < a.n_pairs && base <= z; c += kRows) {
+    const int q = c + tid;
+    int e = -1;
+    const bool lead = q < a.n_pairs && pair_valid(a, q, e) && first[e] == q;
+    const unsigned long long bal = __ballot(lead);
+    if (lane == 0) sh.ball[wave] = bal;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int cw = __popcll(sh.ball[w]);
+      before += (w < wave) ? cw : 0;
+      total += cw;
+    }
+    const int rank = base + before + __popcll(bal & ((1ull << lane) - 1ull));
+    if (lead && rank == z) sh.lead = q;
+    base += total;
+    __syncthreads();  // sh.ball is rewritten by the next chunk
+  }
+  return sh.lead;  // sh.lead is not written again in this launch
+}
+
+// Beyond kLeadExperts experts: workgroup z serves pair z if it leads (a scan
+// of the earlier pairs), so idle workgroups are interleaved with busy ones.
+__device__ int leader_if_first(const KArgs& a, Shared& sh, int z) {
+  const int tid = threadIdx.x;
+  int e;
+  if (!pair_valid(a, z, e)) return -1;
+  e = __builtin_amdgcn_readfirstlane(e);
+  if (tid == 0) sh.flag = 0;
+  __syncthreads();
+  for (int q = tid; q < z; q += kRows) {
+    int eq;
+    if (pair_valid(a, q, eq) && eq == e) sh.flag = 1;
+  }
+  __syncthreads();
+  return sh.flag ? -1 : z;
+}
+
 template <int kMode>
 __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
   __shared__ Shared sh;
   const int tid = threadIdx.x;
-  const int p = blockIdx.z;
+  const int z = blockIdx.z;
   const int split = blockIdx.y;
   const int row = blockIdx.x * kRows + tid;
   const bool row_ok = row < a.n;
 
-  // p is uniform, so are its expert and token; say so to keep descriptors in scalar registers
+  // an invalid pair z gets a row of NaN, whichever workgroup leads below
+  {
+    const int ez = pair_expert(a, z), tz = pair_token(a, z);
+    if ((ez < 0 || ez >= a.n_experts || tz < 0 || tz >= a.n_tokens) && split == 0 && row_ok)
+      a.y[static_cast<int64_t>(z) * a.n + row] = __builtin_nanf("");
+  }
+  // this workgroup leads the z-th leading pair (uniform; -1 if there are fewer)
+  const int p = __builtin_amdgcn_readfirstlane(a.n_experts <= kLeadExperts ? find_leader(a, sh, z)
+                                                                             : leader_if_first(a, sh, z));
+  if (p < 0) return;
   const int e = __builtin_amdgcn_readfirstlane(pair_expert(a, p));
-  const int tk = __builtin_amdgcn_readfirstlane(pair_token(a, p));
-  if (e < 0 || e >= a.n_experts || tk < 0 || tk >= a.n_tokens) {
-    if (split == 0 && row_ok) a.y[static_cast<int64_t>(p) * a.n + row] = __builtin_nanf("");
-    return;
-  }
-  // lead only if no earlier valid pair uses the same expert
-  if (tid == 0) sh.flag = 0;
-  __syncthreads();
-  for (int q = tid; q < p; q += kRows) {
-    const int tq = pair_token(a, q);
-    if (pair_expert(a, q) == e && tq >= 0 && tq < a.n_tokens) sh.flag = 1;
-  }
-  __syncthreads();
-  if (sh.flag) return;
 
   const uint8_t* wexp = a.w + static_cast<int64_t>(e) * a.estride;
   const int b_begin = split * a.bps;

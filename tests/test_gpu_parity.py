@@ -225,6 +225,54 @@ def test_gemv_wide_batch(stq):
                     GEMV_TOL, f"pair {i}")
 
 
+@pytest.mark.parametrize("per_expert", [2, 3, 4, 9])
+def test_gemv_pairs_grouped_by_expert(stq, per_expert):
+    """Pairs sorted by expert (every expert's pairs adjacent) with invalid
+    pairs mixed in: each pair still gets its own expert's product, invalid
+    ones NaN.  (Workgroups serve leading pairs by rank, whatever the pair
+    order.)"""
+    rng = np.random.default_rng(40 + per_expert)
+    n_experts, n, k, n_tokens = 12, 256, 512, 16
+    rb = O.row_bytes(k)
+    table = np.concatenate([O.quantize_rows(S.gaussian_weights(500 + e, n, k), None).reshape(-1)
+                            for e in range(n_experts)])
+    pe = np.repeat(np.arange(n_experts, dtype=np.int32), per_expert)
+    pt = rng.integers(0, n_tokens, pe.size).astype(np.int32)
+    pe[5] = n_experts + 3          # invalid expert
+    pt[-2] = -1                    # invalid token
+    xb, xf = S.bf16_normal(rng, (n_tokens, k))
+    y = host(stq.gemv(dev(table), n * rb, n_experts, n, k, dev(xb.view(np.int16)).view(torch.bfloat16),
+                      dev(pe), dev(pt)))
+    for i, (e, t) in enumerate(zip(pe, pt)):
+        if not (0 <= e < n_experts and 0 <= t < n_tokens):
+            assert np.all(np.isnan(y[i])), i
+            continue
+        raw = table[e * n * rb:(e + 1) * n * rb]
+        check_close(y[i], O.gemv(raw, n, k, xf[t]), O.tolerance_scale(raw, n, k, xf[t])[0], GEMV_TOL, f"pair {i}")
+
+
+def test_gemv_more_experts_than_the_lds_leader_table(stq):
+    """20000 experts (beyond what the in-LDS first-pair table holds): the
+    per-pair leader scan serves them; shared, invalid and far experts."""
+    n_experts, n, k, n_tokens = 20000, 64, 256, 5
+    rb = O.row_bytes(k)
+    used = {0: 1, 7: 2, 19999: 3, 12345: 4}
+    table = np.zeros(n_experts * n * rb, dtype=np.uint8)
+    for e, seed in used.items():
+        table[e * n * rb:(e + 1) * n * rb] = O.quantize_rows(S.gaussian_weights(600 + seed, n, k), None).reshape(-1)
+    pe = np.array([7, 19999, 7, 0, 12345, 20000, 19999, 7], dtype=np.int32)
+    pt = np.array([0, 1, 2, 3, 4, 0, 0, 1], dtype=np.int32)
+    xb, xf = S.bf16_normal(np.random.default_rng(8), (n_tokens, k))
+    y = host(stq.gemv(dev(table), n * rb, n_experts, n, k, dev(xb.view(np.int16)).view(torch.bfloat16),
+                      dev(pe), dev(pt)))
+    for i, (e, t) in enumerate(zip(pe, pt)):
+        if e >= n_experts:
+            assert np.all(np.isnan(y[i])), i
+            continue
+        raw = table[e * n * rb:(e + 1) * n * rb]
+        check_close(y[i], O.gemv(raw, n, k, xf[t]), O.tolerance_scale(raw, n, k, xf[t])[0], GEMV_TOL, f"pair {i}")
+
+
 # ---------------------------------------------------------------------------
 # grouped GEMM
 # ---------------------------------------------------------------------------
