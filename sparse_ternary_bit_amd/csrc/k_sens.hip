@@ -27,18 +27,45 @@ constexpr int kDPitch = kSensK + 2;   // doubles per staged D row (272 B: confli
 constexpr int kXPitch = kSensK + 4;   // floats per staged x row (144 B)
 
 // ---------------------------------------------------------------------------
-// H_kk = sum over calibration rows, in row order, of x_ik^2 (fp64)
+// H_kk = sum over calibration rows of x_ik^2 (fp64).  A workgroup owns 32
+// columns; its 8 row slices (slice s takes rows s, s+8, s+16, ...) add their
+// rows in order, then the 8 slice sums are added in slice order: a fixed
+// order, independent of scheduling.
 // ---------------------------------------------------------------------------
+constexpr int kHdCols = 32;
+constexpr int kHdSlices = 8;
+
 __global__ __launch_bounds__(256) void hdiag_kernel(const float* __restrict__ x, int64_t n_cal, int64_t k,
                                                     double* __restrict__ hd) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (c >= k) return;
+  __shared__ double part[kHdSlices][kHdCols];
+  const int tx = threadIdx.x & (kHdCols - 1), ty = threadIdx.x / kHdCols;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kHdCols + tx;
   double s = 0.0;
-  for (int64_t i = 0; i < n_cal; ++i) {
-    const double v = static_cast<double>(x[i * k + c]);
-    s += v * v;
+  if (c < k) {
+    int64_t i = ty;
+    for (; i + 3 * kHdSlices < n_cal; i += 4 * kHdSlices) {
+      const double v0 = static_cast<double>(x[i * k + c]);
+      const double v1 = static_cast<double>(x[(i + kHdSlices) * k + c]);
+      const double v2 = static_cast<double>(x[(i + 2 * kHdSlices) * k + c]);
+      const double v3 = static_cast<double>(x[(i + 3 * kHdSlices) * k + c]);
+      s += v0 * v0;
+      s += v1 * v1;
+      s += v2 * v2;
+      s += v3 * v3;
+    }
+    for (; i < n_cal; i += kHdSlices) {
+      const double v = static_cast<double>(x[i * k + c]);
+      s += v * v;
+    }
   }
-  hd[c] = s;
+  part[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && c < k) {
+    double t = part[0][tx];
+#pragma unroll
+    for (int j = 1; j < kHdSlices; ++j) t += part[j][tx];
+    hd[c] = t;
+  }
 }
 
 // One staged float4 slot: D = w - w_hat in fp64 (zero for rows past the
@@ -279,7 +306,8 @@ hipError_t launch_layer_errors(const float* w, const float* w_hat, int64_t n_row
   double* partial = hd + k;
   const int rtiles = static_cast<int>((n_rows + kSensRows - 1) / kSensRows);
   const int ctiles = static_cast<int>(cal_tiles(n_cal));
-  hipLaunchKernelGGL(hdiag_kernel, dim3(static_cast<unsigned>((k + 255) / 256)), dim3(256), 0, s, x, n_cal, k, hd);
+  hipLaunchKernelGGL(hdiag_kernel, dim3(static_cast<unsigned>((k + kHdCols - 1) / kHdCols)), dim3(256), 0, s, x, n_cal,
+                     k, hd);
   const int64_t groups = (rtiles + 7) / 8;
   hipLaunchKernelGGL(layer_errors_kernel, dim3(static_cast<unsigned>(groups * 8 * ctiles)), dim3(256), 0, s, w,
                      w_hat, static_cast<int>(n_rows), k, x, static_cast<int>(n_cal), hd, partial, err_diag, ctiles);
