@@ -108,7 +108,8 @@ def test_layer_errors_exact_zero_and_repeatable(stq):
 def test_layer_errors_full_size_sampled_rows(stq):
     """4096 x 7168 weights (one expert's gate/up matrix) with 512 calibration
     rows, the benchmark's shape, encoded on the GPU with the calibration
-    imatrix; the oracle encodes sampled rows itself and scores them."""
+    imatrix; the oracle encodes sampled rows itself and scores them.  The
+    2-bit stand-in of the same weights is checked on the sampled rows."""
     n, k, n_cal = 4096, 7168, 512
     w = S.gaussian_weights(41, n, k)
     x = S.paired_channel_layer(42, 1, k, n_cal, sign=1.0, coupling=0.5)[1]
@@ -122,6 +123,9 @@ def test_layer_errors_full_size_sampled_rows(stq):
     ws_hat = O.dequantize_rows(O.quantize_rows(ws, q), len(rows), k)
     check_errors(full[rows], diag[rows], ws, ws_hat, x, "full size")
     assert np.all(np.isfinite(full)) and np.all(full > 0) and np.all(diag > 0)
+    # the 2-bit stand-in at the same size, sampled rows bit for bit
+    q2 = host(stq.q2_roundtrip(wd))
+    assert np.array_equal(q2[rows].view(np.uint32), O.q2_roundtrip(ws).view(np.uint32))
 
 
 def test_allocation_study_matches_oracle(stq):
