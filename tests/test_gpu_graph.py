@@ -112,3 +112,23 @@ def test_moe_ffn_under_graph(stq):
         x.copy_(S.torch_bf16_normal(113 + r, (T, d_model)))
         pw.copy_(torch.from_numpy(S.routing_weights(114 + r, T, top_k)).cuda())
     _replay_matches_eager(cap, eager, refresh, y)
+
+
+def test_layer_errors_under_graph(stq):
+    # the H diagonal and per-tile partial sums live in the scratch arena
+    n, k, n_cal = 130, 512, 70
+    w = S.torch_expert_weights(130, 0, n, k)
+    x = S.torch_expert_weights(131, 0, n_cal, k, std=1.0)
+    w_hat = stq.q2_roundtrip(w)
+    ef = torch.empty(n, dtype=torch.float64, device="cuda")
+    ed = torch.empty(n, dtype=torch.float64, device="cuda")
+    both = torch.empty(2 * n, dtype=torch.float64, device="cuda")
+    cap = lambda: (stq.layer_errors(w, w_hat, x, ef, ed), both[:n].copy_(ef), both[n:].copy_(ed))
+
+    def eager():
+        f, d = stq.layer_errors(w, w_hat, x)
+        return torch.cat([f, d])
+
+    def refresh(r):
+        x.copy_(S.torch_expert_weights(132 + r, 0, n_cal, k, std=1.0))
+    _replay_matches_eager(cap, eager, refresh, both)
