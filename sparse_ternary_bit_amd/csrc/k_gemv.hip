@@ -360,7 +360,7 @@ __device__ int leader_if_first(const KArgs& a, Shared& sh, int z) {
 }
 
 template <int kMode>
-__global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
+__device__ __forceinline__ void gemv_main(const KArgs& a) {
   __shared__ Shared sh;
   const int tid = threadIdx.x;
   const int z = blockIdx.z;
@@ -409,6 +409,19 @@ __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
     }
     __syncthreads();  // sh.pairs is rewritten by the next gather
   }
+}
+
+template <int kMode>
+__global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
+  gemv_main<kMode>(a);
+}
+
+// SwiGLU rows (the FFN's down projection) build their tables through an
+// exponential and need more registers; held to 128 VGPRs, two workgroups
+// still fit per CU (unbounded they take 139 and one).  The bf16 and fp32
+// variants fit without the bound and run faster without it.
+__global__ __launch_bounds__(kRows, 4) void gemv_kernel_swiglu(KArgs a) {
+  gemv_main<kXSwiGLU>(a);
 }
 
 // y[p, r] = sum over splits s, in order, of partial[s, p, r], for valid pairs.
@@ -520,7 +533,7 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
   const dim3 grid(ntiles, pl.splits, a.n_pairs);
   switch (ga.x_mode) {
     case kXBF16: hipLaunchKernelGGL((gemv_kernel<kXBF16>), grid, dim3(kRows), 0, s, a); break;
-    case kXSwiGLU: hipLaunchKernelGGL((gemv_kernel<kXSwiGLU>), grid, dim3(kRows), 0, s, a); break;
+    case kXSwiGLU: hipLaunchKernelGGL(gemv_kernel_swiglu, grid, dim3(kRows), 0, s, a); break;
     default: hipLaunchKernelGGL((gemv_kernel<kXF32>), grid, dim3(kRows), 0, s, a); break;
   }
   hipError_t err = hipGetLastError();
