@@ -251,6 +251,30 @@ def test_gemv_pairs_grouped_by_expert(stq, per_expert):
         check_close(y[i], O.gemv(raw, n, k, xf[t]), O.tolerance_scale(raw, n, k, xf[t])[0], GEMV_TOL, f"pair {i}")
 
 
+@pytest.mark.parametrize("order", ["token_major", "sorted_by_expert"])
+def test_gemv_pairs_beyond_one_scan_chunk(stq, order):
+    """1500 pairs (three 512-pair chunks of the on-device leader ranking and
+    pair gathering) over 40 experts, several passes per expert, in token
+    order and sorted by expert; every pair against the oracle."""
+    n_experts, n, k, n_tokens = 40, 128, 512, 300
+    rb = O.row_bytes(k)
+    table = np.concatenate([O.quantize_rows(S.gaussian_weights(700 + e, n, k), None).reshape(-1)
+                            for e in range(n_experts)])
+    rng = np.random.default_rng(77)
+    pe = np.concatenate([rng.choice(n_experts, 5, replace=False) for _ in range(n_tokens)]).astype(np.int32)
+    pt = np.repeat(np.arange(n_tokens, dtype=np.int32), 5)
+    if order == "sorted_by_expert":
+        perm = np.argsort(pe, kind="stable")
+        pe, pt = pe[perm], pt[perm]
+    xb, xf = S.bf16_normal(rng, (n_tokens, k))
+    y = host(stq.gemv(dev(table), n * rb, n_experts, n, k, dev(xb.view(np.int16)).view(torch.bfloat16),
+                      dev(pe), dev(pt)))
+    for i in range(len(pe)):
+        raw = table[pe[i] * n * rb:(pe[i] + 1) * n * rb]
+        check_close(y[i], O.gemv(raw, n, k, xf[pt[i]]), O.tolerance_scale(raw, n, k, xf[pt[i]])[0],
+                    GEMV_TOL, f"pair {i}")
+
+
 def test_gemv_more_experts_than_the_lds_leader_table(stq):
     """20000 experts (beyond what the in-LDS first-pair table holds): the
     per-pair leader scan serves them; shared, invalid and far experts."""
