@@ -193,8 +193,12 @@ __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, flo
     const uint32_t Q = blk.qs[w];
     const uint32_t Hs = blk.qh[w >> 2] << (6 - 2 * (w & 3));
     // byte j of cl / cu = 4 * code of group 8w+j / 8w+4+j
-    const uint32_t cl = ((Q << 2) & 0x3C3C3C3Cu) | (Hs & 0x40404040u);
-    const uint32_t cu = ((Q >> 2) & 0x3C3C3C3Cu) | ((Hs >> 1) & 0x40404040u);
+    uint32_t cl = ((Q << 2) & 0x3C3C3C3Cu) | (Hs & 0x40404040u);
+    uint32_t cu = ((Q >> 2) & 0x3C3C3C3Cu) | ((Hs >> 1) & 0x40404040u);
+    // Opaque to the optimiser: knowing bits 0, 1 and 7 of every byte are
+    // zero, it would shrink a byte extract's mask to 0x7C and emit a shift
+    // and an AND; hidden, each extract below is one v_bfe_u32.
+    asm("" : "+v"(cl), "+v"(cu));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t ol = __builtin_amdgcn_ubfe(cl, 8 * j, 8);
