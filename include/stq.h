@@ -125,7 +125,12 @@ stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, floa
  *   y         [n_pairs, n] fp32
  * Accumulation is fp32 with products exact; the summation order is fixed,
  * so repeated calls give identical bits.  Splitting k across workgroups uses
- * the per-device scratch arena (see the conventions above). */
+ * the per-device scratch arena (see the conventions above).  The k split,
+ * and the parting of an expert with several tokens into up to one k range
+ * per token, are chosen per call from the shapes and the device's CU count;
+ * the environment variable STQ_GEMV_PLAN="s,p" (1 <= s <= k/256 splits,
+ * 1 <= p <= 8 parts) replaces that choice, for tuning and tests.  Results
+ * meet the same tolerance under every plan; their bits depend on the plan. */
 stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts,
                     int64_t n, int64_t k, const void* x, int x_dtype, int64_t x_row_stride,
                     int64_t n_tokens, const int32_t* pair_expert, const int32_t* pair_token,

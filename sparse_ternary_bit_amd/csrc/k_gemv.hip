@@ -30,14 +30,20 @@
 // two blocks ahead, in the order they are consumed.
 //
 // k split: the blocks of a row may be split over several workgroups (chosen
-// per call from the expected number of active experts, see plan_gemv); each
-// writes fp32 partial sums to scratch and a second small kernel adds them in
-// split order, so the result does not depend on scheduling.
+// per call from the expected number of active experts, see plan_gemv), and
+// an expert with several tokens has each split's blocks parted further, one
+// part per token up to a cap, so that every workgroup costs about the same;
+// split workgroups write fp32 partial sums to scratch and a second small
+// kernel adds them in k order, so the result does not depend on scheduling.
 #include <math.h>
 
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <utility>
+#include <vector>
 
 #include "stq_device.hpp"
 #include "stq_launch.hpp"
@@ -67,7 +73,9 @@ struct KArgs {
   float* y;
   int bps;         // blocks per split
   int splits;
-  float* partial;  // [splits, n_pairs, n] when splits > 1
+  int max_sub;     // an expert with m tokens splits each k range into min(m, max_sub) parts
+  float* partial;  // [splits * max_sub, n_pairs, n] when a pair's output is split
+  int32_t* pair_sub;  // per pair: its expert's part count (read by the reduction)
   int ppt;         // without pair_token: pair q uses token q / ppt
   int64_t ff;      // SwiGLU activations: offset of the "up" half in a row
 };
@@ -82,8 +90,11 @@ struct Shared {
   int mc;
   int next;
   int lead;
+  int sub;
+  int nsub;
   int flag;
   unsigned long long ball[kWaves];
+  int wsum[kWaves];
 };
 
 // Collect up to kMT pairs with expert e and a valid token, from `cursor` on,
@@ -295,13 +306,17 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
 
 // A pair leads when its token is valid and no earlier valid pair names the
 // same expert; the leading pair of an expert collects all of that expert's
-// pairs (gather above).  Workgroup z serves the z-th leading pair in pair
-// order, so the workgroups with work are the first ones launched whatever
-// the order of the pairs: workgroups are dealt to the shader engines of an
-// XCD round robin, and a periodic pattern of idle workgroups (pairs sorted by
-// expert, say, with four pairs per expert) would otherwise put all the work
-// on one of them.
-constexpr int kLeadExperts = static_cast<int>(sizeof(Shared::tab) / sizeof(int));
+// pairs (gather above).  An expert with m pairs is served by min(m, max_sub)
+// units, each taking one part of the workgroup's k range for all m tokens,
+// so a unit costs about what a one-token expert costs whatever m is.  Units
+// are numbered by leading pair in pair order (an expert's parts in k order)
+// and workgroup z serves unit z, so the workgroups with work are the first
+// ones launched whatever the order of the pairs: workgroups are dealt to the
+// shader engines of an XCD round robin, and a periodic pattern of idle
+// workgroups (pairs sorted by expert, say, with four pairs per expert) would
+// otherwise put all the work on one of them.  There are at most as many
+// units as valid pairs, so a grid of n_pairs workgroups covers them.
+constexpr int kLeadExperts = static_cast<int>(sizeof(Shared::tab) / (2 * sizeof(int)));
 
 __device__ __forceinline__ bool pair_valid(const KArgs& a, int q, int& e) {
   e = pair_expert(a, q);
@@ -309,18 +324,28 @@ __device__ __forceinline__ bool pair_valid(const KArgs& a, int q, int& e) {
   return e >= 0 && e < a.n_experts && t >= 0 && t < a.n_tokens;
 }
 
-// With at most kLeadExperts experts: the first valid pair of every expert by
-// an LDS atomic minimum (in the table space, unused until the tables are
-// built), then a running count of leading pairs in pair order until the z-th.
-__device__ int find_leader(const KArgs& a, Shared& sh, int z) {
+// With at most kLeadExperts experts: the first valid pair and the pair count
+// of every expert by LDS atomics (in the table space, unused until the tables
+// are built), then a running sum of the leading pairs' unit counts in pair
+// order until it passes z.  Leaves the part index and count in sh.sub and
+// sh.nsub.
+__device__ int find_unit(const KArgs& a, Shared& sh, int z) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int* first = reinterpret_cast<int*>(&sh.tab[0][0]);
-  for (int e = tid; e < a.n_experts; e += kRows) first[e] = 0x7FFFFFFF;
+  int* count = first + a.n_experts;
+  for (int e = tid; e < a.n_experts; e += kRows) {
+    first[e] = 0x7FFFFFFF;
+    count[e] = 0;
+  }
   if (tid == 0) sh.lead = -1;
   __syncthreads();
+  const bool parts = a.max_sub > 1;
   for (int q = tid; q < a.n_pairs; q += kRows) {
     int e;
-    if (pair_valid(a, q, e)) atomicMin(&first[e], q);
+    if (pair_valid(a, q, e)) {
+      atomicMin(&first[e], q);
+      if (parts) atomicAdd(&count[e], 1);
+    }
   }
   __syncthreads();
   int base = 0;
@@ -328,32 +353,54 @@ __device__ int find_leader(const KArgs& a, Shared& sh, int z) {
     const int q = c + tid;
     int e = -1;
     const bool lead = q < a.n_pairs && pair_valid(a, q, e) && first[e] == q;
-    const unsigned long long bal = __ballot(lead);
-    if (lane == 0) sh.ball[wave] = bal;
+    const int units = lead ? (parts ? min(count[e], a.max_sub) : 1) : 0;
+    // inclusive prefix sum of the unit counts over the wavefront (a ballot
+    // count when every count is 0 or 1), then over the waves
+    int incl;
+    if (parts) {
+      incl = units;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+    } else {
+      incl = __popcll(__ballot(lead) & (~0ull >> (63 - lane)));
+    }
+    if (lane == 63) sh.wsum[wave] = incl;
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const int cw = __popcll(sh.ball[w]);
-      before += (w < wave) ? cw : 0;
-      total += cw;
+      const int sw = sh.wsum[w];
+      before += (w < wave) ? sw : 0;
+      total += sw;
     }
-    const int rank = base + before + __popcll(bal & ((1ull << lane) - 1ull));
-    if (lead && rank == z) sh.lead = q;
+    const int first_unit = base + before + incl - units;
+    if (units > 0 && z >= first_unit && z < first_unit + units) {
+      sh.lead = q;
+      sh.sub = z - first_unit;
+      sh.nsub = units;
+    }
     base += total;
-    __syncthreads();  // sh.ball is rewritten by the next chunk
+    __syncthreads();  // sh.wsum is rewritten by the next chunk
   }
-  return sh.lead;  // sh.lead is not written again in this launch
+  return sh.lead;  // sh.lead, sh.sub and sh.nsub are not written again in this launch
 }
 
-// Beyond kLeadExperts experts: workgroup z serves pair z if it leads (a scan
-// of the earlier pairs), so idle workgroups are interleaved with busy ones.
+// Beyond kLeadExperts experts: workgroup z serves pair z, as its expert's
+// only unit, if it leads (a scan of the earlier pairs), so idle workgroups
+// are interleaved with busy ones.
 __device__ int leader_if_first(const KArgs& a, Shared& sh, int z) {
   const int tid = threadIdx.x;
   int e;
   if (!pair_valid(a, z, e)) return -1;
   e = __builtin_amdgcn_readfirstlane(e);
-  if (tid == 0) sh.flag = 0;
+  if (tid == 0) {
+    sh.flag = 0;
+    sh.sub = 0;
+    sh.nsub = 1;
+  }
   __syncthreads();
   for (int q = tid; q < z; q += kRows) {
     int eq;
@@ -378,15 +425,25 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
     if ((ez < 0 || ez >= a.n_experts || tz < 0 || tz >= a.n_tokens) && split == 0 && row_ok)
       a.y[static_cast<int64_t>(z) * a.n + row] = __builtin_nanf("");
   }
-  // this workgroup leads the z-th leading pair (uniform; -1 if there are fewer)
-  const int p = __builtin_amdgcn_readfirstlane(a.n_experts <= kLeadExperts ? find_leader(a, sh, z)
+  // this workgroup serves unit z: part `sub` of `nsub` of the expert of leading pair p
+  // (uniform; p = -1 if there are fewer units)
+  const int p = __builtin_amdgcn_readfirstlane(a.n_experts <= kLeadExperts ? find_unit(a, sh, z)
                                                                              : leader_if_first(a, sh, z));
   if (p < 0) return;
   const int e = __builtin_amdgcn_readfirstlane(pair_expert(a, p));
+  const int sub = __builtin_amdgcn_readfirstlane(sh.sub);
+  const int nsub = __builtin_amdgcn_readfirstlane(sh.nsub);
 
   const uint8_t* wexp = a.w + static_cast<int64_t>(e) * a.estride;
-  const int b_begin = split * a.bps;
-  const int b_end = min(a.nb, b_begin + a.bps);
+  // blocks of split `split`, then part `sub` of them (a part is empty only when the last
+  // split is shorter than nsub: its workgroup then adds zeros to its slot)
+  const int s_begin = split * a.bps;
+  const int s_len = min(a.nb, s_begin + a.bps) - s_begin;
+  const int b_begin = s_begin + (sub * s_len) / nsub;
+  const int b_end = s_begin + ((sub + 1) * s_len) / nsub;
+  // partial slot of this unit: k order is split-major, part-minor
+  const int n_slots = a.splits * nsub;
+  const int slot = split * nsub + sub;
 
   int cursor = p;
   for (;;) {
@@ -406,11 +463,13 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
       for (int m = 0; m < kMT; ++m) {
         if (m < mc) {
           const int64_t q = sh.pairs[m];
-          if (a.splits == 1) a.y[q * a.n + row] = acc[m];
-          else a.partial[(static_cast<int64_t>(split) * a.n_pairs + q) * a.n + row] = acc[m];
+          if (n_slots == 1) a.y[q * a.n + row] = acc[m];
+          else a.partial[(static_cast<int64_t>(slot) * a.n_pairs + q) * a.n + row] = acc[m];
         }
       }
     }
+    // the reduction learns each pair's part count from the first unit of its expert
+    if (a.pair_sub && split == 0 && sub == 0 && blockIdx.x == 0 && tid < mc) a.pair_sub[sh.pairs[tid]] = nsub;
     __syncthreads();  // sh.pairs is rewritten by the next gather
   }
 }
@@ -428,11 +487,14 @@ __global__ __launch_bounds__(kRows, 4) void gemv_kernel_swiglu(KArgs a) {
   gemv_main<kXSwiGLU>(a);
 }
 
-// y[p, r] = sum over splits s, in order, of partial[s, p, r], for valid pairs.
-// The loads of 16 splits are issued before their adds, so the loop pays one
-// memory latency per 16 splits; the additions stay in split order.
+// y[p, r] = sum over the pair's slots s, in order, of partial[s, p, r], for
+// valid pairs whose output is split (splits x the pair's part count > 1; the
+// others were written directly).  The loads of 16 slots are issued before
+// their adds, so the loop pays one memory latency per 16 slots; the additions
+// stay in slot (= k) order.
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partial, int splits,
-                                                            int64_t plane, const int32_t* __restrict__ pe,
+                                                            const int32_t* __restrict__ pair_sub, int64_t plane,
+                                                            const int32_t* __restrict__ pe,
                                                             const int32_t* __restrict__ pt, int ppt, int n_experts,
                                                             int n_tokens, int n, float* __restrict__ y) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -441,10 +503,12 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   const int e = pe ? pe[p] : 0;
   const int t = pt ? pt[p] : p / ppt;
   if (e < 0 || e >= n_experts || t < 0 || t >= n_tokens) return;  // the GEMV wrote NaN there
+  const int slots = pair_sub ? splits * pair_sub[p] : splits;
+  if (slots == 1) return;  // the GEMV wrote y itself
   constexpr int kBatch = 16;
   float s = 0.0f;
   int sp = 0;
-  for (; sp + kBatch <= splits; sp += kBatch) {
+  for (; sp + kBatch <= slots; sp += kBatch) {
     float v[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) v[j] = partial[static_cast<int64_t>(sp + j) * plane + i];
@@ -454,10 +518,10 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   float v[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    if (sp + j < splits) v[j] = partial[static_cast<int64_t>(sp + j) * plane + i];
+    if (sp + j < slots) v[j] = partial[static_cast<int64_t>(sp + j) * plane + i];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    if (sp + j < splits) s += v[j];
+    if (sp + j < slots) s += v[j];
   y[i] = s;
 }
 
@@ -478,38 +542,136 @@ static int device_cus() {
   return cus;
 }
 
+// Work of one pass over a block, relative to a one-token pass, for a pass
+// of 1..4 tokens (measured on a full layer with every expert given the same
+// token count: 1, 1.6, 1.96 and 2.47); an expert with m tokens makes
+// floor(m / 4) four-token passes and one pass of the rest.
+static double block_cost(int m) {
+  constexpr double kPass[5] = {0.0, 1.0, 1.6, 1.96, 2.47};
+  return (m / 4) * kPass[4] + kPass[m % 4];
+}
+
 // k split: the kernel keeps two workgroups resident per CU (its LDS tables),
-// so workgroups run in rounds of 2 * CUs.  The number of leading workgroups
-// is estimated from the pairs, assuming they spread over the experts
-// (expected distinct experts of n_pairs uniform draws).  Of the split counts,
-// take the one with the least rounds x (blocks per workgroup + ~2 blocks of
-// fixed cost: launch, pair scan, table and pipeline fill); ties go to fewer
-// splits.
-GemvPlan plan_gemv(const GemvArgs& a) {
-  GemvPlan pl{};
+// so workgroups run in rounds of 2 * CUs.  Each split's blocks are parted
+// further by token count (an expert with m pairs takes min(m, sub) units,
+// sub <= max_sub keeping at least kMinSubBlocks blocks a part), so heavy
+// experts need not hold the last round.  For each (splits, max_sub) the
+// time is estimated in one-token block passes from the expected experts per
+// token count (pairs spread uniformly over the experts, m binomial): the
+// units' work plus kUnitCost per unit (launch, pair scan, table and pipeline
+// fill) spread over the resident slots, but no less than the longest unit,
+// plus a fraction of the longest unit for the tail, plus the fp32 partial
+// sums' write and read at the rate the slots stream weights.  The constants
+// fit measured times of a 256-expert 4096 x 7168 layer at 4 to 512 pairs.
+// Plans whose partial sums pass kMaxPartialBytes are not taken (one k split
+// and one part per expert needs none).
+constexpr int kMinSubBlocks = 4;
+constexpr int kMaxSub = 8;
+constexpr double kUnitCost = 3.5;
+constexpr double kTailShare = 0.2;
+constexpr double kMaxPartialBytes = 1024.0 * 1024.0 * 1024.0;
+
+static void estimate_plan(const GemvArgs& a, int cus, int& best_splits, int& best_bps, int& best_sub) {
   const int nb = static_cast<int>(a.k / kQK);
-  const int64_t ntiles = (a.n + kRows - 1) / kRows;
-  const double ne = static_cast<double>(a.n_experts);
-  const double distinct = std::min(static_cast<double>(a.n_pairs),
-                                   ne * (1.0 - std::pow(1.0 - 1.0 / ne, static_cast<double>(a.n_pairs))));
-  const double base_wgs = std::max(1.0, std::ceil(distinct) * static_cast<double>(ntiles));
-  const double slots = 2.0 * device_cus();
-  int best_splits = 1, best_bps = nb;
-  double best_cost = 0.0;
+  const double ntiles = static_cast<double>((a.n + kRows - 1) / kRows);
+  const bool parts_ok = a.n_experts <= kLeadExperts;  // beyond, an expert is one unit
+  const double slots = 2.0 * cus;
+  // expected number of experts with exactly m pairs, over m within 8 standard
+  // deviations of the mean (binomial in log space, so nothing underflows)
+  std::vector<std::pair<int, double>> cnt;
+  const double np = static_cast<double>(a.n_pairs), ne = static_cast<double>(a.n_experts);
+  if (a.n_experts <= 1) {
+    cnt.emplace_back(static_cast<int>(a.n_pairs), 1.0);
+  } else {
+    const double p = 1.0 / ne, mean = np * p, sd = std::sqrt(np * p * (1.0 - p));
+    const int lo = std::max(1, static_cast<int>(std::floor(mean - 8.0 * sd)) - 1);
+    const int hi = static_cast<int>(std::min(np, std::ceil(mean + 8.0 * sd) + 8.0));
+    const double lg_n = std::lgamma(np + 1.0), lp = std::log(p), lq = std::log1p(-p);
+    for (int m = lo; m <= hi; ++m) {
+      const double lpm = lg_n - std::lgamma(m + 1.0) - std::lgamma(np - m + 1.0) + m * lp + (np - m) * lq;
+      const double c = ne * std::exp(lpm);
+      if (c > 1e-9) cnt.emplace_back(m, c);
+    }
+  }
+  best_splits = 1;
+  best_bps = nb;
+  best_sub = 1;
+  double best_cost = -1.0;
   for (int splits = 1; splits <= nb; ++splits) {
     const int bps = (nb + splits - 1) / splits;
     if ((nb + bps - 1) / bps != splits) continue;  // the same split under another count
-    const double rounds = std::ceil(base_wgs * splits / slots);
-    const double cost = rounds * (bps + 2.0);
-    if (splits == 1 || cost < best_cost) {
-      best_cost = cost;
-      best_splits = splits;
-      best_bps = bps;
+    const int sub_cap = parts_ok ? std::max(1, std::min(kMaxSub, bps / kMinSubBlocks)) : 1;
+    for (int max_sub = 1; max_sub <= sub_cap; ++max_sub) {
+      const double n_slots = static_cast<double>(splits) * max_sub;
+      if (n_slots > 1.0 && n_slots * np * static_cast<double>(a.n) * 4.0 > kMaxPartialBytes) continue;
+      double work = 0.0, longest = 0.0, partial_sums = 0.0;
+      for (const auto& [m, count] : cnt) {
+        const int parts = std::min(m, max_sub);
+        const double c = block_cost(m) * bps;
+        work += count * (c + kUnitCost * parts);
+        if (count >= 0.3) longest = std::max(longest, c / parts + kUnitCost);
+        if (splits * parts > 1) partial_sums += m * count * splits * parts;  // pair outputs through scratch
+      }
+      work *= ntiles * splits;
+      const double traffic = partial_sums * static_cast<double>(a.n) * 8.0 / (slots * kRows * kBlockBytes);
+      const double cost = std::max(work / slots, longest) + kTailShare * longest + traffic;
+      if (best_cost < 0.0 || cost < best_cost * (1.0 - 1e-9)) {
+        best_cost = cost;
+        best_splits = splits;
+        best_bps = bps;
+        best_sub = max_sub;
+      }
+    }
+  }
+}
+
+// The estimate depends only on the shapes and the CU count; decode loops
+// repeat a few shapes, so each host thread keeps its last 16 answers.
+GemvPlan plan_gemv(const GemvArgs& a) {
+  struct Entry {
+    int64_t n_pairs, n_experts, n, k;
+    int cus, splits, bps, sub;
+  };
+  thread_local Entry cache[16];
+  thread_local int cache_used = 0, cache_next = 0;
+  const int cus = device_cus();
+  const int nb = static_cast<int>(a.k / kQK);
+  const bool parts_ok = a.n_experts <= kLeadExperts;
+  int best_splits = 0, best_bps = 0, best_sub = 0;
+  for (int i = 0; i < cache_used; ++i) {
+    const Entry& c = cache[i];
+    if (c.n_pairs == a.n_pairs && c.n_experts == a.n_experts && c.n == a.n && c.k == a.k && c.cus == cus) {
+      best_splits = c.splits;
+      best_bps = c.bps;
+      best_sub = c.sub;
+      break;
+    }
+  }
+  if (best_splits == 0) {
+    estimate_plan(a, cus, best_splits, best_bps, best_sub);
+    cache[cache_next] = Entry{a.n_pairs, a.n_experts, a.n, a.k, cus, best_splits, best_bps, best_sub};
+    cache_next = (cache_next + 1) % 16;
+    cache_used = std::min(cache_used + 1, 16);
+  }
+  GemvPlan pl{};
+  // STQ_GEMV_PLAN="splits,max_sub" replaces the estimate (tuning and tests;
+  // max_sub may exceed the blocks of a split, leaving some parts empty)
+  if (const char* ev = std::getenv("STQ_GEMV_PLAN")) {
+    int sp = 0, ms = 0;
+    if (std::sscanf(ev, "%d,%d", &sp, &ms) == 2 && sp >= 1 && sp <= nb && ms >= 1 && ms <= kMaxSub) {
+      best_bps = (nb + sp - 1) / sp;
+      best_splits = (nb + best_bps - 1) / best_bps;
+      best_sub = parts_ok ? ms : 1;
     }
   }
   pl.blocks_per_split = best_bps;
   pl.splits = best_splits;
-  if (pl.splits > 1) pl.partial_bytes = static_cast<int64_t>(pl.splits) * a.n_pairs * a.n * 4;
+  pl.max_sub = best_sub;
+  const int64_t n_slots = static_cast<int64_t>(pl.splits) * pl.max_sub;
+  if (n_slots > 1) {
+    pl.partial_floats = n_slots * a.n_pairs * a.n;
+    pl.partial_bytes = (pl.partial_floats * 4 + 255) / 256 * 256 + (pl.max_sub > 1 ? a.n_pairs * 4 : 0);
+  }
   return pl;
 }
 
@@ -530,7 +692,11 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
   a.y = ga.y;
   a.bps = pl.blocks_per_split;
   a.splits = pl.splits;
+  a.max_sub = pl.max_sub;
   a.partial = static_cast<float*>(partial);
+  a.pair_sub = pl.max_sub > 1
+                   ? reinterpret_cast<int32_t*>(static_cast<char*>(partial) + (pl.partial_floats * 4 + 255) / 256 * 256)
+                   : nullptr;
   a.ppt = ga.pairs_per_token > 0 ? static_cast<int>(ga.pairs_per_token) : 1;
   a.ff = ga.ff;
   const int ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
@@ -541,11 +707,11 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
     default: hipLaunchKernelGGL((gemv_kernel<kXF32>), grid, dim3(kRows), 0, s, a); break;
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || pl.splits == 1) return err;
+  if (err != hipSuccess || pl.partial_bytes == 0) return err;
   const int64_t plane = ga.n_pairs * ga.n;
   const int64_t grid2 = (plane + 255) / 256;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3(static_cast<unsigned>(grid2)), dim3(256), 0, s, a.partial,
-                     pl.splits, plane, a.pe, a.pt, a.ppt, a.n_experts, a.n_tokens, a.n, a.y);
+                     pl.splits, a.pair_sub, plane, a.pe, a.pt, a.ppt, a.n_experts, a.n_tokens, a.n, a.y);
   return hipGetLastError();
 }
 

@@ -150,7 +150,7 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
                    x_row_stride, n_tokens, pair_expert, pair_token, n_pairs, y, 1, 0};
   const stq::GemvPlan pl = stq::plan_gemv(ga);
   void* partial = nullptr;
-  const stq_status st = arena_get(pl.splits > 1 ? pl.partial_bytes : 0, &partial, "stq_gemv: scratch");
+  const stq_status st = arena_get(pl.partial_bytes, &partial, "stq_gemv: scratch");
   if (st != STQ_OK) return st;
   hipError_t le = stq::launch_gemv(ga, pl, partial, reinterpret_cast<hipStream_t>(stream));
   if (le != hipSuccess) return hip_fail(le, "stq_gemv launch");
@@ -182,7 +182,7 @@ stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_b
   stq::GemvArgs g2{w_down, down_stride_bytes, n_experts, d_model, d_ff, nullptr, 2, 2 * d_ff, P,
                    pair_expert, nullptr, P, nullptr, 1, d_ff};
   const stq::GemvPlan p1 = stq::plan_gemv(g1), p2 = stq::plan_gemv(g2);
-  const int64_t part = round256(std::max(p1.splits > 1 ? p1.partial_bytes : 0, p2.splits > 1 ? p2.partial_bytes : 0));
+  const int64_t part = round256(std::max(p1.partial_bytes, p2.partial_bytes));
   const int64_t gu_bytes = round256(P * 2 * d_ff * 4);
   const int64_t z_bytes = round256(P * d_model * 4);
   void* base = nullptr;

@@ -31,10 +31,13 @@ struct GemvArgs {
 };
 
 // Scratch needed by launch_gemv for the chosen k split (bytes, 0 if none),
-// and the launch itself; with splits > 1, `partial` holds partial_bytes bytes.
+// and the launch itself; with partial_bytes > 0, `partial` holds that many
+// bytes (fp32 partial sums, then one int per pair).
 struct GemvPlan {
   int splits;          // k split across workgroups
   int blocks_per_split;
+  int max_sub;         // most parts a split's blocks are cut into for a many-token expert
+  int64_t partial_floats;
   int64_t partial_bytes;
 };
 GemvPlan plan_gemv(const GemvArgs& a);

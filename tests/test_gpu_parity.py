@@ -225,6 +225,37 @@ def test_gemv_wide_batch(stq):
                     GEMV_TOL, f"pair {i}")
 
 
+@pytest.mark.parametrize("plan", [None, "1,2", "1,8", "2,3", "3,4", "5,8", "10,1"])
+def test_gemv_token_parts_match_oracle(stq, monkeypatch, plan):
+    """Experts with 0-8 tokens under forced (k splits, part cap) plans: an
+    expert with m tokens has each split's blocks parted min(m, cap) ways and
+    the parts' partial sums added in k order.  k = 2560 (10 blocks), so
+    "3,4" (splits of 4, 4, 2 blocks) and "5,8" (2 blocks a split) leave
+    some parts empty; pairs shuffled, one invalid."""
+    if plan is not None:
+        monkeypatch.setenv("STQ_GEMV_PLAN", plan)
+    rng = np.random.default_rng(61)
+    counts = [1, 2, 3, 4, 5, 8, 0]
+    n_experts, n, k, n_tokens = len(counts), 192, 2560, 12
+    rb = O.row_bytes(k)
+    table = np.concatenate([O.quantize_rows(S.gaussian_weights(800 + e, n, k), None).reshape(-1)
+                            for e in range(n_experts)])
+    pe = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)] + [np.array([n_experts], np.int32)])
+    pt = np.concatenate([rng.choice(n_tokens, c, replace=False) for c in counts] + [np.array([0])]).astype(np.int32)
+    perm = rng.permutation(pe.size)
+    pe, pt = pe[perm], pt[perm]
+    xb, xf = S.bf16_normal(rng, (n_tokens, k))
+    y = host(stq.gemv(dev(table), n * rb, n_experts, n, k, dev(xb.view(np.int16)).view(torch.bfloat16),
+                      dev(pe), dev(pt)))
+    for i, (e, t) in enumerate(zip(pe, pt)):
+        if e >= n_experts:
+            assert np.all(np.isnan(y[i])), i
+            continue
+        raw = table[e * n * rb:(e + 1) * n * rb]
+        check_close(y[i], O.gemv(raw, n, k, xf[t]), O.tolerance_scale(raw, n, k, xf[t])[0], GEMV_TOL,
+                    f"plan {plan} pair {i} (expert {e})")
+
+
 @pytest.mark.parametrize("per_expert", [2, 3, 4, 9])
 def test_gemv_pairs_grouped_by_expert(stq, per_expert):
     """Pairs sorted by expert (every expert's pairs adjacent) with invalid
