@@ -333,13 +333,13 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int* first = reinterpret_cast<int*>(&sh.tab[0][0]);
   int* count = first + a.n_experts;
+  const bool parts = a.max_sub > 1;  // else every leading pair is one unit and counts are not needed
   for (int e = tid; e < a.n_experts; e += kRows) {
     first[e] = 0x7FFFFFFF;
-    count[e] = 0;
+    if (parts) count[e] = 0;
   }
   if (tid == 0) sh.lead = -1;
   __syncthreads();
-  const bool parts = a.max_sub > 1;
   for (int q = tid; q < a.n_pairs; q += kRows) {
     int e;
     if (pair_valid(a, q, e)) {
@@ -431,16 +431,17 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
                                                                              : leader_if_first(a, sh, z));
   if (p < 0) return;
   const int e = __builtin_amdgcn_readfirstlane(pair_expert(a, p));
-  const int sub = __builtin_amdgcn_readfirstlane(sh.sub);
-  const int nsub = __builtin_amdgcn_readfirstlane(sh.nsub);
+  const bool parts = a.max_sub > 1;
+  const int sub = parts ? __builtin_amdgcn_readfirstlane(sh.sub) : 0;
+  const int nsub = parts ? __builtin_amdgcn_readfirstlane(sh.nsub) : 1;
 
   const uint8_t* wexp = a.w + static_cast<int64_t>(e) * a.estride;
   // blocks of split `split`, then part `sub` of them (a part is empty only when the last
   // split is shorter than nsub: its workgroup then adds zeros to its slot)
   const int s_begin = split * a.bps;
   const int s_len = min(a.nb, s_begin + a.bps) - s_begin;
-  const int b_begin = s_begin + (sub * s_len) / nsub;
-  const int b_end = s_begin + ((sub + 1) * s_len) / nsub;
+  const int b_begin = parts ? s_begin + (sub * s_len) / nsub : s_begin;
+  const int b_end = parts ? s_begin + ((sub + 1) * s_len) / nsub : s_begin + s_len;
   // partial slot of this unit: k order is split-major, part-minor
   const int n_slots = a.splits * nsub;
   const int slot = split * nsub + sub;
@@ -489,22 +490,25 @@ __global__ __launch_bounds__(kRows, 4) void gemv_kernel_swiglu(KArgs a) {
 
 // y[p, r] = sum over the pair's slots s, in order, of partial[s, p, r], for
 // valid pairs whose output is split (splits x the pair's part count > 1; the
-// others were written directly).  The loads of 16 slots are issued before
-// their adds, so the loop pays one memory latency per 16 slots; the additions
-// stay in slot (= k) order.
+// others were written directly).  Workgroup (x, p) covers rows 256x.. of
+// pair p, so the pair's checks and slot count are uniform.  The loads of 16
+// slots are issued before their adds, so the loop pays one memory latency
+// per 16 slots; the additions stay in slot (= k) order.
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partial, int splits,
-                                                            const int32_t* __restrict__ pair_sub, int64_t plane,
+                                                            const int32_t* __restrict__ pair_sub, int n_pairs,
                                                             const int32_t* __restrict__ pe,
                                                             const int32_t* __restrict__ pt, int ppt, int n_experts,
                                                             int n_tokens, int n, float* __restrict__ y) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= plane) return;
-  const int p = static_cast<int>(i / n);
+  const int p = blockIdx.y;
   const int e = pe ? pe[p] : 0;
   const int t = pt ? pt[p] : p / ppt;
   if (e < 0 || e >= n_experts || t < 0 || t >= n_tokens) return;  // the GEMV wrote NaN there
   const int slots = pair_sub ? splits * pair_sub[p] : splits;
   if (slots == 1) return;  // the GEMV wrote y itself
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= n) return;
+  const int64_t plane = static_cast<int64_t>(n_pairs) * n;
+  const int64_t i = static_cast<int64_t>(p) * n + r;
   constexpr int kBatch = 16;
   float s = 0.0f;
   int sp = 0;
@@ -708,10 +712,9 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || pl.partial_bytes == 0) return err;
-  const int64_t plane = ga.n_pairs * ga.n;
-  const int64_t grid2 = (plane + 255) / 256;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3(static_cast<unsigned>(grid2)), dim3(256), 0, s, a.partial,
-                     pl.splits, a.pair_sub, plane, a.pe, a.pt, a.ppt, a.n_experts, a.n_tokens, a.n, a.y);
+  const dim3 grid2(static_cast<unsigned>((ga.n + 255) / 256), static_cast<unsigned>(ga.n_pairs));
+  hipLaunchKernelGGL(reduce_splits_kernel, grid2, dim3(256), 0, s, a.partial, pl.splits, a.pair_sub, a.n_pairs,
+                     a.pe, a.pt, a.ppt, a.n_experts, a.n_tokens, a.n, a.y);
   return hipGetLastError();
 }
 
