@@ -57,6 +57,14 @@ constexpr int kMT = 4;                     // tokens per pass
 constexpr int kTabBytes = kGroups * 32 * 4;
 constexpr int kTokStride = kTabBytes + 16; // token tables apart by a non-multiple of 256 bytes
 constexpr int kBufBytes = kMT * kTokStride;
+// With bf16 activations, passes of 2 or more tokens tabulate two tokens to
+// an 8-byte entry: group g's 256-byte table at g * 256, the second pair's
+// tables kPairStride further (16-byte aligned and not a multiple of 512, so
+// the compiler keeps the two pairs' reads apart instead of fusing them into
+// one 16-byte read that it then waits on read by read).
+constexpr int kPairTab = kGroups * 32 * 8;
+constexpr int kPairStride = kPairTab + 16;
+static_assert(kPairStride + kPairTab <= kBufBytes, "two pair tables fit a buffer");
 
 struct KArgs {
   const uint8_t* w;
@@ -134,6 +142,8 @@ __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
       if (mc < kMT) next = base + kRows;
       sh.mc = mc;
       sh.next = next;
+      // unused token slots repeat the last token found (a 3-token pass may run as a 4-token one)
+      for (int m = mc; m < kMT; ++m) sh.toks[m] = mc > 0 ? sh.toks[mc - 1] : 0;
     }
     __syncthreads();
     if (sh.mc >= kMT) break;
@@ -192,6 +202,81 @@ __device__ __forceinline__ void build_entries(const XGroup<kMode>& xg, int z, ch
   o[1] = make_float4(-e3, -e2, -e1, -e0);
 }
 
+// Entries 8z..8z+7 of one group for a token pair, interleaved: entry c
+// holds the first token's sum at 8c and the second's at 8c + 4.
+template <int kMode>
+__device__ __forceinline__ void build_pair_entries(const XGroup<kMode>& xa, const XGroup<kMode>& xb, int z,
+                                                   char* dst) {
+  float ea[8], eb[8];
+  {
+    const float x0 = xa.get(0), x1 = xa.get(1), x2 = xa.get(2), x3 = xa.get(3);
+    const float a = (z == 0) ? x1 : x0, b = (z <= 1) ? x2 : x1, c = (z <= 2) ? x3 : x2;
+    const float u0 = a + b, u1 = b - a;
+    ea[0] = u0 + c; ea[1] = u1 + c; ea[2] = c - u1; ea[3] = c - u0;
+  }
+  {
+    const float x0 = xb.get(0), x1 = xb.get(1), x2 = xb.get(2), x3 = xb.get(3);
+    const float a = (z == 0) ? x1 : x0, b = (z <= 1) ? x2 : x1, c = (z <= 2) ? x3 : x2;
+    const float u0 = a + b, u1 = b - a;
+    eb[0] = u0 + c; eb[1] = u1 + c; eb[2] = c - u1; eb[3] = c - u0;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ea[4 + i] = -ea[3 - i];
+    eb[4 + i] = -eb[3 - i];
+  }
+  float4* o = reinterpret_cast<float4*>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = make_float4(ea[2 * i], eb[2 * i], ea[2 * i + 1], eb[2 * i + 1]);
+}
+
+// Pair tables: sum over the 64 groups of one block for MC = 2 or 4 tokens,
+// one 8-byte read per group and token pair (an LDS read issues at the same
+// rate for 4 and 8 bytes, so a token pair costs one read slot instead of
+// two); a word's reads are all issued before its adds, and each token's
+// sums are added in group order, as in block_dot.
+template <int MC>
+__device__ __forceinline__ void block_dot_pairs(const char* tab, const Block& blk, float (&acc)[kMT]) {
+  constexpr int kNP = MC / 2;
+  const float d = half_bits_to_float(blk.d16);
+  float bs[MC];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) bs[m] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint32_t Q = blk.qs[w];
+    const uint32_t H = blk.qh[w >> 2];
+    const int i = w & 3;
+    // byte j of cl / cu = 8 * code of group 8w+j / 8w+4+j (select bit at bit 7)
+    uint32_t cl = ((Q << 3) & 0x78787878u) | ((H << (7 - 2 * i)) & 0x80808080u);
+    uint32_t cu = ((Q >> 1) & 0x78787878u) | ((H << (6 - 2 * i)) & 0x80808080u);
+    asm("" : "+v"(cl), "+v"(cu));
+    float2 vl[4][kNP], vu[4][kNP];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t ol = __builtin_amdgcn_ubfe(cl, 8 * j, 8);
+      const uint32_t ou = __builtin_amdgcn_ubfe(cu, 8 * j, 8);
+#pragma unroll
+      for (int p = 0; p < kNP; ++p) {
+        vl[j][p] = *reinterpret_cast<const float2*>(tab + ol + (p * kPairStride + (8 * w + j) * 256));
+        vu[j][p] = *reinterpret_cast<const float2*>(tab + ou + (p * kPairStride + (8 * w + 4 + j) * 256));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int p = 0; p < kNP; ++p) {
+        bs[2 * p] += vl[j][p].x;
+        bs[2 * p + 1] += vl[j][p].y;
+        bs[2 * p] += vu[j][p].x;
+        bs[2 * p + 1] += vu[j][p].y;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MC; ++m) acc[m] = fmaf(d, bs[m], acc[m]);
+}
+
 // Sum over the 64 groups of one block of table[code], for MC tokens.
 template <int MC>
 __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, float (&acc)[kMT]) {
@@ -232,21 +317,27 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // table items of this thread: item i = 256*m + 4*g + z, items tid and tid + 512
-  constexpr int kItems = 256 * MC;
+  // Table items of this thread.  Pair tables (bf16 activations, MC = 2 or 4):
+  // item (token pair tid / 256, group g, zero lane z), one per thread.  Else
+  // item i = 256*m + 4*g + z for token m, items tid and tid + 512.
+  constexpr bool kPair = kMode == kXBF16 && MC >= 2;
+  static_assert(!kPair || MC == 2 || MC == 4, "pair tables take 2 or 4 tokens");
+  constexpr int kItems = kPair ? 128 * MC : 256 * MC;
   const int it_g = (tid >> 2) & 63, it_z = tid & 3;
   const int m0 = tid >> 8, m1 = m0 + 2;
-  const bool has0 = tid < kItems, has1 = tid + kRows < kItems;
+  const bool has0 = tid < kItems, has1 = !kPair && tid + kRows < kItems;
   int tok[MC];
 #pragma unroll
   for (int m = 0; m < MC; ++m) tok[m] = __builtin_amdgcn_readfirstlane(sh.toks[m]);
+  // single tables: tok0 / tok1 are the tokens of items tid / tid + 512;
+  // pair tables: the two tokens of this thread's pair
   int tok0 = 0, tok1 = 0;
 #pragma unroll
   for (int m = 0; m < MC; ++m) {
-    if (m == m0) tok0 = tok[m];
-    if (m == m1) tok1 = tok[m];
+    if (kPair ? m == 2 * m0 : m == m0) tok0 = tok[m];
+    if (kPair ? m == 2 * m0 + 1 : m == m1) tok1 = tok[m];
   }
-  const int tab_off0 = m0 * kTokStride + it_g * 128 + it_z * 32;
+  const int tab_off0 = kPair ? m0 * kPairStride + it_g * 256 + it_z * 64 : m0 * kTokStride + it_g * 128 + it_z * 32;
   const int tab_off1 = m1 * kTokStride + it_g * 128 + it_z * 32;
 
 #pragma unroll
@@ -262,12 +353,19 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   };
   auto load_x = [&](XGroup<kMode> (&x)[2], int b) {
     const int64_t col = static_cast<int64_t>(b) * kQK + 4 * it_g;
-    if (has0) x[0].load(a, tok0, col);
+    if (has0) {
+      x[0].load(a, tok0, col);
+      if (kPair) x[1].load(a, tok1, col);
+    }
     if (has1) x[1].load(a, tok1, col);
   };
   auto build = [&](const XGroup<kMode> (&x)[2], char* t) {
-    if (has0) build_entries<kMode>(x[0], it_z, t + tab_off0);
-    if (has1) build_entries<kMode>(x[1], it_z, t + tab_off1);
+    if constexpr (kPair) {
+      if (has0) build_pair_entries<kMode>(x[0], x[1], it_z, t + tab_off0);
+    } else {
+      if (has0) build_entries<kMode>(x[0], it_z, t + tab_off0);
+      if (has1) build_entries<kMode>(x[1], it_z, t + tab_off1);
+    }
   };
   // 42*(b*valid + lane) is 2 mod 4 exactly when b*valid + lane is odd
   const bool lane_odd = (lane & 1) != 0;
@@ -285,7 +383,8 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
     if (b + 1 < b_end) build(xnext, tnext);
     if (b + 2 < b_end) load_w(wcur, b + 2);
     if (b + 3 < b_end) load_x(xnext, b + 3);
-    block_dot<MC>(tcur, blk, acc);
+    if constexpr (kPair) block_dot_pairs<MC>(tcur, blk, acc);
+    else block_dot<MC>(tcur, blk, acc);
     __syncthreads();  // table b+1 is complete and every thread is done with table b
   };
   {
@@ -456,7 +555,10 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
     switch (mc) {
       case 1: run_chunk<kMode, 1>(a, sh, wexp, b_begin, b_end, acc); break;
       case 2: run_chunk<kMode, 2>(a, sh, wexp, b_begin, b_end, acc); break;
-      case 3: run_chunk<kMode, 3>(a, sh, wexp, b_begin, b_end, acc); break;
+      case 3:  // pair tables take 3 tokens as 4 (the fourth repeats the third, its sums unused)
+        if constexpr (kMode == kXBF16) run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc);
+        else run_chunk<kMode, 3>(a, sh, wexp, b_begin, b_end, acc);
+        break;
       default: run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc); break;
     }
     if (row_ok) {
@@ -547,11 +649,11 @@ static int device_cus() {
 }
 
 // Work of one pass over a block, relative to a one-token pass, for a pass
-// of 1..4 tokens (measured on a full layer with every expert given the same
-// token count: 1, 1.6, 1.96 and 2.47); an expert with m tokens makes
-// floor(m / 4) four-token passes and one pass of the rest.
+// of 1..4 tokens (measured with bf16 activations on a full layer, every
+// expert given the same token count: 1, 1.45, 2.1 and 2.18); an expert with
+// m tokens makes floor(m / 4) four-token passes and one pass of the rest.
 static double block_cost(int m) {
-  constexpr double kPass[5] = {0.0, 1.0, 1.6, 1.96, 2.47};
+  constexpr double kPass[5] = {0.0, 1.0, 1.45, 2.1, 2.18};
   return (m / 4) * kPass[4] + kPass[m % 4];
 }
 
