@@ -155,8 +155,8 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
  *   pair_expert int32, pair_weight fp32 [n_tokens*top_k], token-major
  *   y          fp32 [n_tokens, d_model]
  * Both projections run through the GEMV above (pairs sharing an expert are
- * batched), the activation inside the down projection's operand load;
- * intermediates live in the scratch arena.  A pair whose expert is outside
+ * batched), with h formed once per element between them; intermediates
+ * live in the scratch arena.  A pair whose expert is outside
  * [0, n_experts) makes its token's row NaN.  At most 65535 pairs per call. */
 stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_bytes, const uint8_t* w_down,
                               int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,

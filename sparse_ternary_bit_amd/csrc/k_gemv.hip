@@ -85,7 +85,6 @@ struct KArgs {
   float* partial;  // [splits * max_sub, n_pairs, n] when a pair's output is split
   int32_t* pair_sub;  // per pair: its expert's part count (read by the reduction)
   int ppt;         // without pair_token: pair q uses token q / ppt
-  int64_t ff;      // SwiGLU activations: offset of the "up" half in a row
 };
 
 __device__ __forceinline__ int pair_expert(const KArgs& a, int q) { return a.pe ? a.pe[q] : 0; }
@@ -151,13 +150,12 @@ __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
 }
 
 // Activations of one group (4 values) of one token at column `col`, by
-// source kind: fp32 rows, bf16 rows, or SwiGLU of fp32 gate/up rows
-// (value = silu(row[col]) * row[ff + col], silu(v) = v / (1 + exp(-v))).
-enum XMode { kXF32 = 0, kXBF16 = 1, kXSwiGLU = 2 };
+// source kind: fp32 rows or bf16 rows.
+enum XMode { kXF32 = 0, kXBF16 = 1 };
 
 template <int kMode>
 struct XGroup {
-  static constexpr int kWords = kMode == kXBF16 ? 2 : (kMode == kXSwiGLU ? 8 : 4);
+  static constexpr int kWords = kMode == kXBF16 ? 2 : 4;
   uint32_t v[kWords];
   __device__ __forceinline__ void load(const KArgs& a, int tok, int64_t col) {
     if constexpr (kMode == kXBF16) {
@@ -168,18 +166,11 @@ struct XGroup {
       const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.x) + tok * a.xstride + col);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = p[i];
-      if constexpr (kMode == kXSwiGLU) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[4 + i] = p[a.ff + i];
-      }
     }
   }
   __device__ __forceinline__ float get(int j) const {
     if constexpr (kMode == kXBF16) {
       return __uint_as_float(j & 1 ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16));
-    } else if constexpr (kMode == kXSwiGLU) {
-      const float g = __uint_as_float(v[j]);
-      return g / (1.0f + expf(-g)) * __uint_as_float(v[4 + j]);
     } else {
       return __uint_as_float(v[j]);
     }
@@ -582,14 +573,6 @@ __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
   gemv_main<kMode>(a);
 }
 
-// SwiGLU rows (the FFN's down projection) build their tables through an
-// exponential and need more registers; held to 128 VGPRs, two workgroups
-// still fit per CU (unbounded they take 139 and one).  The bf16 and fp32
-// variants fit without the bound and run faster without it.
-__global__ __launch_bounds__(kRows, 4) void gemv_kernel_swiglu(KArgs a) {
-  gemv_main<kXSwiGLU>(a);
-}
-
 // y[p, r] = sum over the pair's slots s, in order, of partial[s, p, r], for
 // valid pairs whose output is split (splits x the pair's part count > 1; the
 // others were written directly).  Workgroup (x, p) covers rows 256x.. of
@@ -804,12 +787,10 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
                    ? reinterpret_cast<int32_t*>(static_cast<char*>(partial) + (pl.partial_floats * 4 + 255) / 256 * 256)
                    : nullptr;
   a.ppt = ga.pairs_per_token > 0 ? static_cast<int>(ga.pairs_per_token) : 1;
-  a.ff = ga.ff;
   const int ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
   const dim3 grid(ntiles, pl.splits, a.n_pairs);
   switch (ga.x_mode) {
     case kXBF16: hipLaunchKernelGGL((gemv_kernel<kXBF16>), grid, dim3(kRows), 0, s, a); break;
-    case kXSwiGLU: hipLaunchKernelGGL(gemv_kernel_swiglu, grid, dim3(kRows), 0, s, a); break;
     default: hipLaunchKernelGGL((gemv_kernel<kXF32>), grid, dim3(kRows), 0, s, a); break;
   }
   hipError_t err = hipGetLastError();

@@ -147,7 +147,7 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
   if (x_dtype == STQ_X_BF16 && (x_row_stride % 2)) return fail(STQ_E_ALIGN, "stq_gemv: bf16 x_row_stride must be even");
 
   stq::GemvArgs ga{w_table, expert_stride_bytes, n_experts, n, k, x, x_dtype == STQ_X_BF16 ? 1 : 0,
-                   x_row_stride, n_tokens, pair_expert, pair_token, n_pairs, y, 1, 0};
+                   x_row_stride, n_tokens, pair_expert, pair_token, n_pairs, y, 1};
   const stq::GemvPlan pl = stq::plan_gemv(ga);
   void* partial = nullptr;
   const stq_status st = arena_get(pl.partial_bytes, &partial, "stq_gemv: scratch");
@@ -176,27 +176,32 @@ stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_b
     return fail(STQ_E_ALIGN, "stq_moe_ffn_decode: x, pair arrays or y not 4-byte aligned");
 
   const int64_t P = n_tokens * top_k;
-  // gate/up GEMV of every pair's token, then the down GEMV of SwiGLU(gate/up row)
+  // gate/up GEMV of every pair's token, SwiGLU of each gate/up row, then the
+  // down GEMV of every pair's activation row
   stq::GemvArgs g1{w_gate_up, gate_up_stride_bytes, n_experts, 2 * d_ff, d_model, x, 1, d_model, n_tokens,
-                   pair_expert, nullptr, P, nullptr, top_k, 0};
-  stq::GemvArgs g2{w_down, down_stride_bytes, n_experts, d_model, d_ff, nullptr, 2, 2 * d_ff, P,
-                   pair_expert, nullptr, P, nullptr, 1, d_ff};
+                   pair_expert, nullptr, P, nullptr, top_k};
+  stq::GemvArgs g2{w_down, down_stride_bytes, n_experts, d_model, d_ff, nullptr, 0, d_ff, P,
+                   pair_expert, nullptr, P, nullptr, 1};
   const stq::GemvPlan p1 = stq::plan_gemv(g1), p2 = stq::plan_gemv(g2);
   const int64_t part = round256(std::max(p1.partial_bytes, p2.partial_bytes));
   const int64_t gu_bytes = round256(P * 2 * d_ff * 4);
+  const int64_t h_bytes = round256(P * d_ff * 4);
   const int64_t z_bytes = round256(P * d_model * 4);
   void* base = nullptr;
-  const stq_status st = arena_get(part + gu_bytes + z_bytes, &base, "stq_moe_ffn_decode: scratch");
+  const stq_status st = arena_get(part + gu_bytes + h_bytes + z_bytes, &base, "stq_moe_ffn_decode: scratch");
   if (st != STQ_OK) return st;
   char* b = static_cast<char*>(base);
   float* gu = reinterpret_cast<float*>(b + part);
-  float* z = reinterpret_cast<float*>(b + part + gu_bytes);
+  float* h = reinterpret_cast<float*>(b + part + gu_bytes);
+  float* z = reinterpret_cast<float*>(b + part + gu_bytes + h_bytes);
   g1.y = gu;
-  g2.x = gu;
+  g2.x = h;
   g2.y = z;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = stq::launch_gemv(g1, p1, b, s);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: gate/up launch");
+  e = stq::launch_swiglu(gu, P, d_ff, h, s);
+  if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: SwiGLU launch");
   e = stq::launch_gemv(g2, p2, b, s);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: down launch");
   e = stq::launch_combine(z, pair_weight, n_tokens, top_k, d_model, y, s);

@@ -19,7 +19,7 @@ struct GemvArgs {
   int64_t n;
   int64_t k;
   const void* x;
-  int x_mode;               // 0 fp32 rows, 1 bf16 rows, 2 SwiGLU of fp32 gate/up rows
+  int x_mode;               // 0 fp32 rows, 1 bf16 rows
   int64_t x_row_stride;     // elements
   int64_t n_tokens;
   const int32_t* pair_expert;
@@ -27,7 +27,6 @@ struct GemvArgs {
   int64_t n_pairs;
   float* y;
   int64_t pairs_per_token;  // used only without pair_token (0 means 1)
-  int64_t ff;               // x_mode 2: column offset of the "up" half of a row
 };
 
 // Scratch needed by launch_gemv for the chosen k split (bytes, 0 if none),
@@ -42,6 +41,10 @@ struct GemvPlan {
 };
 GemvPlan plan_gemv(const GemvArgs& a);
 hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& plan, void* partial, hipStream_t s);
+
+// h[p, c] = silu(gu[p, c]) * gu[p, d_ff + c], silu(v) = v / (1 + exp(-v)),
+// for gu [n_pairs, 2*d_ff] and h [n_pairs, d_ff] fp32 (d_ff a multiple of 4)
+hipError_t launch_swiglu(const float* gu, int64_t n_pairs, int64_t d_ff, float* h, hipStream_t s);
 
 // y[t, :] = sum over k < top_k, in order, of w[t*top_k + k] * z[t*top_k + k, :]
 hipError_t launch_combine(const float* z, const float* w, int64_t n_tokens, int64_t top_k, int64_t n, float* y,
