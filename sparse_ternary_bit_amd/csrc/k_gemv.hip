@@ -18,9 +18,12 @@
 // code (already scaled by 4) and, per token, one LDS read with the group's
 // table offset as an immediate plus one fp32 add; the block's fp16 scale
 // multiplies the block sum.  All threads of a wavefront read the same group's
-// 128-byte table at once, so the reads are bank-conflict free.  Tables are
-// double-buffered: while block b is summed from one buffer, block b+1's table
-// is built into the other, one barrier per block.
+// 128-byte table at once, so the reads are bank-conflict free.  With bf16
+// activations and 2-4 tokens in a pass, two tokens share an 8-byte table
+// entry and one 8-byte read serves both (an LDS read issues at the same rate
+// for 4 and 8 bytes, and the table reads bound the extra tokens of a pass).
+// Tables are double-buffered: while block b is summed from one buffer, block
+// b+1's table is built into the other, one barrier per block.
 //
 // Weights: the matrix is stored in 64-row tiles, block-major inside a tile,
 // so a wavefront's 64 rows of block b are one contiguous 2688-byte run.  Each
@@ -177,48 +180,48 @@ struct XGroup {
   }
 };
 
-// Table entries 8z..8z+7 of one group for zero lane z.  Entry 8z+m is the sum
-// over the three kept lanes (in order) of -x or +x as bit r of m says.
+// Signed sums of one group for zero lane z, with a, b, c its three other
+// lanes in order: e[m] (m = 0..3) is a + b + c with a negated when bit 0 of
+// m is set and b negated when bit 1 is.  Table entries 8z+m for m = 4..7
+// (c negated as well) are the negations -e[7-m].
 template <int kMode>
-__device__ __forceinline__ void build_entries(const XGroup<kMode>& xg, int z, char* dst) {
+__device__ __forceinline__ void signed_sums(const XGroup<kMode>& xg, int z, float (&e)[4]) {
   const float x0 = xg.get(0), x1 = xg.get(1), x2 = xg.get(2), x3 = xg.get(3);
   const float a = (z == 0) ? x1 : x0;
   const float b = (z <= 1) ? x2 : x1;
   const float c = (z <= 2) ? x3 : x2;
   const float u0 = a + b;   // +a +b
   const float u1 = b - a;   // -a +b
-  const float e0 = u0 + c, e1 = u1 + c, e2 = c - u1, e3 = c - u0;
-  float4* o = reinterpret_cast<float4*>(dst);
-  o[0] = make_float4(e0, e1, e2, e3);
-  o[1] = make_float4(-e3, -e2, -e1, -e0);
+  e[0] = u0 + c;
+  e[1] = u1 + c;
+  e[2] = c - u1;
+  e[3] = c - u0;
 }
 
-// Entries 8z..8z+7 of one group for a token pair, interleaved: entry c
-// holds the first token's sum at 8c and the second's at 8c + 4.
+// Table entries 8z..8z+7 of one group for zero lane z.  Entry 8z+m is the sum
+// over the three kept lanes (in order) of -x or +x as bit r of m says.
+template <int kMode>
+__device__ __forceinline__ void build_entries(const XGroup<kMode>& xg, int z, char* dst) {
+  float e[4];
+  signed_sums<kMode>(xg, z, e);
+  float4* o = reinterpret_cast<float4*>(dst);
+  o[0] = make_float4(e[0], e[1], e[2], e[3]);
+  o[1] = make_float4(-e[3], -e[2], -e[1], -e[0]);
+}
+
+// The same entries for a token pair, interleaved: entry c holds the first
+// token's sum at 8c and the second's at 8c + 4.
 template <int kMode>
 __device__ __forceinline__ void build_pair_entries(const XGroup<kMode>& xa, const XGroup<kMode>& xb, int z,
                                                    char* dst) {
-  float ea[8], eb[8];
-  {
-    const float x0 = xa.get(0), x1 = xa.get(1), x2 = xa.get(2), x3 = xa.get(3);
-    const float a = (z == 0) ? x1 : x0, b = (z <= 1) ? x2 : x1, c = (z <= 2) ? x3 : x2;
-    const float u0 = a + b, u1 = b - a;
-    ea[0] = u0 + c; ea[1] = u1 + c; ea[2] = c - u1; ea[3] = c - u0;
-  }
-  {
-    const float x0 = xb.get(0), x1 = xb.get(1), x2 = xb.get(2), x3 = xb.get(3);
-    const float a = (z == 0) ? x1 : x0, b = (z <= 1) ? x2 : x1, c = (z <= 2) ? x3 : x2;
-    const float u0 = a + b, u1 = b - a;
-    eb[0] = u0 + c; eb[1] = u1 + c; eb[2] = c - u1; eb[3] = c - u0;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ea[4 + i] = -ea[3 - i];
-    eb[4 + i] = -eb[3 - i];
-  }
+  float ea[4], eb[4];
+  signed_sums<kMode>(xa, z, ea);
+  signed_sums<kMode>(xb, z, eb);
   float4* o = reinterpret_cast<float4*>(dst);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = make_float4(ea[2 * i], eb[2 * i], ea[2 * i + 1], eb[2 * i + 1]);
+  o[0] = make_float4(ea[0], eb[0], ea[1], eb[1]);
+  o[1] = make_float4(ea[2], eb[2], ea[3], eb[3]);
+  o[2] = make_float4(-ea[3], -eb[3], -ea[2], -eb[2]);
+  o[3] = make_float4(-ea[1], -eb[1], -ea[0], -eb[0]);
 }
 
 // Pair tables: sum over the 64 groups of one block for MC = 2 or 4 tokens,
@@ -241,7 +244,7 @@ __device__ __forceinline__ void block_dot_pairs(const char* tab, const Block& bl
     // byte j of cl / cu = 8 * code of group 8w+j / 8w+4+j (select bit at bit 7)
     uint32_t cl = ((Q << 3) & 0x78787878u) | ((H << (7 - 2 * i)) & 0x80808080u);
     uint32_t cu = ((Q >> 1) & 0x78787878u) | ((H << (6 - 2 * i)) & 0x80808080u);
-    asm("" : "+v"(cl), "+v"(cu));
+    asm("" : "+v"(cl), "+v"(cu));  // one bit-field extract per code, as in block_dot
     float2 vl[4][kNP], vu[4][kNP];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
