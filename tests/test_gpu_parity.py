@@ -256,6 +256,31 @@ def test_gemv_token_parts_match_oracle(stq, monkeypatch, plan):
                     f"plan {plan} pair {i} (expert {e})")
 
 
+@pytest.mark.parametrize("plan", [None, "2,3"])
+def test_gemv_two_token_tables_match_one_token_tables(stq, monkeypatch, plan):
+    """bf16 activations run passes of 2-4 tokens on two-token tables, fp32
+    activations on one-token tables; the table sums and each token's order of
+    adds are the same, so on bf16-representable activations the two paths
+    must agree bit for bit, for experts with 1-8 tokens."""
+    if plan is not None:
+        monkeypatch.setenv("STQ_GEMV_PLAN", plan)
+    rng = np.random.default_rng(63)
+    counts = [1, 2, 3, 4, 5, 6, 7, 8]
+    n_experts, n, k, n_tokens = len(counts), 320, 2560, 10
+    rb = O.row_bytes(k)
+    table = np.concatenate([O.quantize_rows(S.gaussian_weights(900 + e, n, k), None).reshape(-1)
+                            for e in range(n_experts)])
+    pe = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    pt = np.concatenate([rng.choice(n_tokens, c, replace=False) for c in counts]).astype(np.int32)
+    perm = rng.permutation(pe.size)
+    pe, pt = dev(pe[perm]), dev(pt[perm])
+    xb, xf = S.bf16_normal(rng, (n_tokens, k))
+    wt = dev(table)
+    y_bf16 = host(stq.gemv(wt, n * rb, n_experts, n, k, dev(xb.view(np.int16)).view(torch.bfloat16), pe, pt))
+    y_f32 = host(stq.gemv(wt, n * rb, n_experts, n, k, dev(xf), pe, pt))
+    assert np.array_equal(y_bf16.view(np.uint32), y_f32.view(np.uint32))
+
+
 @pytest.mark.parametrize("per_expert", [2, 3, 4, 9])
 def test_gemv_pairs_grouped_by_expert(stq, per_expert):
     """Pairs sorted by expert (every expert's pairs adjacent) with invalid
