@@ -579,41 +579,43 @@ __global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
 // y[p, r] = sum over the pair's slots s, in order, of partial[s, p, r], for
 // valid pairs whose output is split (splits x the pair's part count > 1; the
 // others were written directly).  Workgroup (x, p) covers rows 256x.. of
-// pair p, so the pair's checks and slot count are uniform.  The loads of 16
-// slots are issued before their adds, so the loop pays one memory latency
-// per 16 slots; the additions stay in slot (= k) order.
+// pair p, so the pair's checks and slot count are uniform.  The first 16 of
+// the max_slots allocated slots are loaded before the pair's ids and part
+// count arrive (every allocated slot is in bounds; the ones past the pair's
+// count are not used), so a call with at most 16 slots pays one memory
+// latency for its data; the additions stay in slot (= k) order.
 __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ partial, int splits,
-                                                            const int32_t* __restrict__ pair_sub, int n_pairs,
-                                                            const int32_t* __restrict__ pe,
+                                                            int max_slots, const int32_t* __restrict__ pair_sub,
+                                                            int n_pairs, const int32_t* __restrict__ pe,
                                                             const int32_t* __restrict__ pt, int ppt, int n_experts,
                                                             int n_tokens, int n, float* __restrict__ y) {
   const int p = blockIdx.y;
-  const int e = pe ? pe[p] : 0;
-  const int t = pt ? pt[p] : p / ppt;
-  if (e < 0 || e >= n_experts || t < 0 || t >= n_tokens) return;  // the GEMV wrote NaN there
-  const int slots = pair_sub ? splits * pair_sub[p] : splits;
-  if (slots == 1) return;  // the GEMV wrote y itself
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= n) return;
   const int64_t plane = static_cast<int64_t>(n_pairs) * n;
   const int64_t i = static_cast<int64_t>(p) * n + r;
   constexpr int kBatch = 16;
-  float s = 0.0f;
-  int sp = 0;
-  for (; sp + kBatch <= slots; sp += kBatch) {
-    float v[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) v[j] = partial[static_cast<int64_t>(sp + j) * plane + i];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) s += v[j];
-  }
   float v[kBatch];
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    if (sp + j < slots) v[j] = partial[static_cast<int64_t>(sp + j) * plane + i];
+    if (j < max_slots) v[j] = partial[static_cast<int64_t>(j) * plane + i];
+  const int e = pe ? pe[p] : 0;
+  const int t = pt ? pt[p] : p / ppt;
+  if (e < 0 || e >= n_experts || t < 0 || t >= n_tokens) return;  // the GEMV wrote NaN there
+  const int slots = pair_sub ? splits * pair_sub[p] : splits;
+  if (slots == 1) return;  // the GEMV wrote y itself
+  float s = 0.0f;
 #pragma unroll
   for (int j = 0; j < kBatch; ++j)
-    if (sp + j < slots) s += v[j];
+    if (j < slots) s += v[j];
+  for (int sp = kBatch; sp < slots; sp += kBatch) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (sp + j < slots) v[j] = partial[static_cast<int64_t>(sp + j) * plane + i];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (sp + j < slots) s += v[j];
+  }
   y[i] = s;
 }
 
@@ -799,8 +801,8 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || pl.partial_bytes == 0) return err;
   const dim3 grid2(static_cast<unsigned>((ga.n + 255) / 256), static_cast<unsigned>(ga.n_pairs));
-  hipLaunchKernelGGL(reduce_splits_kernel, grid2, dim3(256), 0, s, a.partial, pl.splits, a.pair_sub, a.n_pairs,
-                     a.pe, a.pt, a.ppt, a.n_experts, a.n_tokens, a.n, a.y);
+  hipLaunchKernelGGL(reduce_splits_kernel, grid2, dim3(256), 0, s, a.partial, pl.splits, pl.splits * pl.max_sub,
+                     a.pair_sub, a.n_pairs, a.pe, a.pt, a.ppt, a.n_experts, a.n_tokens, a.n, a.y);
   return hipGetLastError();
 }
 
