@@ -48,10 +48,67 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 // ---------------------------------------------------------------------------
 // encode: one wavefront per block
 // ---------------------------------------------------------------------------
+// Cross-lane steps of the butterfly.  After the steps of stride < s every
+// lane holds its aligned block of s lanes' result, so the partner block's
+// value may come from any of its lanes: a quad permutation (strides 1, 2), a
+// mirror inside 8 or 16 lanes (strides 4, 8; DPP moves, no LDS round trip),
+// a swizzle inside 32 lanes (stride 16), and lanes 0 and 32 (stride 32).
+// Each step adds (or ORs, or maxes) a lane's own block with its partner's, so
+// every lane ends with the same bits as the xor butterfly.
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // lane l <- 7 - l within 8
+constexpr int kDppMirror = 0x140;       // lane l <- 15 - l within 16
+constexpr int kSwizzleXor16 = 0x401F;   // ds_swizzle bit mode: lane l <- l ^ 16 within 32
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+
+// value of the partner block at butterfly stride s (1, 2, 4, 8 or 16)
+template <int kStride>
+__device__ __forceinline__ uint32_t partner_u32(uint32_t v) {
+  if constexpr (kStride == 1) return dpp_u32<kDppQuadSwap1>(v);
+  else if constexpr (kStride == 2) return dpp_u32<kDppQuadSwap2>(v);
+  else if constexpr (kStride == 4) return dpp_u32<kDppHalfMirror>(v);
+  else if constexpr (kStride == 8) return dpp_u32<kDppMirror>(v);
+  else return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), kSwizzleXor16));
+}
+
+template <int kStride>
+__device__ __forceinline__ double partner_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = partner_u32<kStride>(static_cast<uint32_t>(b));
+  const uint64_t hi = partner_u32<kStride>(static_cast<uint32_t>(b >> 32));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// the halves' values at stride 32 (every lane of a half holds its half's value)
+__device__ __forceinline__ double half_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), lane));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), lane));
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// balanced tree of adjacent pairs over the 64 lanes (same bits in every lane)
 __device__ __forceinline__ double wave_tree_sum(double v) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) v = v + __shfl_xor(v, s, 64);
-  return v;
+  v = v + partner_f64<1>(v);
+  v = v + partner_f64<2>(v);
+  v = v + partner_f64<4>(v);
+  v = v + partner_f64<8>(v);
+  v = v + partner_f64<16>(v);
+  return half_f64(v, 0) + half_f64(v, 32);
+}
+
+__device__ __forceinline__ double wave_max(double v) {
+  v = fmax(v, partner_f64<1>(v));
+  v = fmax(v, partner_f64<2>(v));
+  v = fmax(v, partner_f64<4>(v));
+  v = fmax(v, partner_f64<8>(v));
+  v = fmax(v, partner_f64<16>(v));
+  return fmax(half_f64(v, 0), half_f64(v, 32));
 }
 
 __device__ __forceinline__ double wls_scale(const double (&a)[4], const double (&q)[4], int z) {
@@ -124,9 +181,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     }
     d = wls_scale(a, q, z);
   } else {
-    d = fmax(fmax(a[0], a[1]), fmax(a[2], a[3]));
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) d = fmax(d, __shfl_xor(d, s, 64));
+    d = wave_max(fmax(fmax(a[0], a[1]), fmax(a[2], a[3])));
   }
 
   // fp16 scale: fp64 -> fp32 -> fp16, nearest-even each time, clamped to 65504
@@ -149,10 +204,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   const int g = lane;
   uint32_t qsw = (c & 15u) << (8 * (g & 3) + 4 * ((g >> 2) & 1));
   uint32_t qhw = (c >> 4) << (8 * (g & 3) + ((g >> 2) & 7));
-#pragma unroll
-  for (int s = 1; s < 8; s <<= 1) qsw |= __shfl_xor(qsw, s, 64);
-#pragma unroll
-  for (int s = 1; s < 32; s <<= 1) qhw |= __shfl_xor(qhw, s, 64);
+  qsw |= partner_u32<1>(qsw);  // OR over the 8 lanes of a code word
+  qsw |= partner_u32<2>(qsw);
+  qsw |= partner_u32<4>(qsw);
+  qhw |= partner_u32<1>(qhw);  // OR over the 32 lanes of a select word
+  qhw |= partner_u32<2>(qhw);
+  qhw |= partner_u32<4>(qhw);
+  qhw |= partner_u32<8>(qhw);
+  qhw |= partner_u32<16>(qhw);
 
   // 21 half-words per block: [d | 16 x code half-words | 4 x select half-words]
   const int i = lane;
