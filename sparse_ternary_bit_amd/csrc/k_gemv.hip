@@ -769,7 +769,24 @@ GemvPlan plan_gemv(const GemvArgs& a) {
   return pl;
 }
 
-hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hipStream_t s) {
+static int32_t* pair_sub_of(const GemvPlan& pl, void* partial) {
+  return pl.max_sub > 1
+             ? reinterpret_cast<int32_t*>(static_cast<char*>(partial) + (pl.partial_floats * 4 + 255) / 256 * 256)
+             : nullptr;
+}
+
+GemvPartials gemv_partials(const GemvPlan& pl, void* partial) {
+  GemvPartials g{};
+  if (pl.partial_bytes > 0) {
+    g.partial = static_cast<const float*>(partial);
+    g.splits = pl.splits;
+    g.max_slots = pl.splits * pl.max_sub;
+    g.pair_sub = pair_sub_of(pl, partial);
+  }
+  return g;
+}
+
+hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hipStream_t s, bool reduce) {
   if (ga.n_pairs == 0 || ga.n == 0) return hipSuccess;
   KArgs a{};
   a.w = ga.w_table;
@@ -788,9 +805,7 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
   a.splits = pl.splits;
   a.max_sub = pl.max_sub;
   a.partial = static_cast<float*>(partial);
-  a.pair_sub = pl.max_sub > 1
-                   ? reinterpret_cast<int32_t*>(static_cast<char*>(partial) + (pl.partial_floats * 4 + 255) / 256 * 256)
-                   : nullptr;
+  a.pair_sub = pair_sub_of(pl, partial);
   a.ppt = ga.pairs_per_token > 0 ? static_cast<int>(ga.pairs_per_token) : 1;
   const int ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
   const dim3 grid(ntiles, pl.splits, a.n_pairs);
@@ -799,7 +814,7 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
     default: hipLaunchKernelGGL((gemv_kernel<kXF32>), grid, dim3(kRows), 0, s, a); break;
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || pl.partial_bytes == 0) return err;
+  if (err != hipSuccess || pl.partial_bytes == 0 || !reduce) return err;
   const dim3 grid2(static_cast<unsigned>((ga.n + 255) / 256), static_cast<unsigned>(ga.n_pairs));
   hipLaunchKernelGGL(reduce_splits_kernel, grid2, dim3(256), 0, s, a.partial, pl.splits, pl.splits * pl.max_sub,
                      a.pair_sub, a.n_pairs, a.pe, a.pt, a.ppt, a.n_experts, a.n_tokens, a.n, a.y);

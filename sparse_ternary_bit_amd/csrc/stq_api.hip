@@ -198,13 +198,16 @@ stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_b
   g2.x = h;
   g2.y = z;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = stq::launch_gemv(g1, p1, b, s);
+  // each GEMV's split outputs are added by the next step (SwiGLU, combine)
+  // instead of a reduction launch of its own; the order of the adds is the same
+  hipError_t e = stq::launch_gemv(g1, p1, b, s, false);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: gate/up launch");
-  e = stq::launch_swiglu(gu, P, d_ff, h, s);
+  e = stq::launch_swiglu(gu, stq::gemv_partials(p1, b), pair_expert, n_experts, P, d_ff, h, s);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: SwiGLU launch");
-  e = stq::launch_gemv(g2, p2, b, s);
+  e = stq::launch_gemv(g2, p2, b, s, false);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: down launch");
-  e = stq::launch_combine(z, pair_weight, n_tokens, top_k, d_model, y, s);
+  e = stq::launch_combine(z, stq::gemv_partials(p2, b), pair_expert, n_experts, pair_weight, n_tokens, top_k,
+                                d_model, y, s);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: combine launch");
   return ok();
 }

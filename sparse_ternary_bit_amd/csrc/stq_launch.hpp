@@ -40,15 +40,35 @@ struct GemvPlan {
   int64_t partial_bytes;
 };
 GemvPlan plan_gemv(const GemvArgs& a);
-hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& plan, void* partial, hipStream_t s);
+// reduce = false leaves split outputs in `partial` for the caller to add (see
+// GemvPartials); the GEMV still writes y's rows that are not split and the
+// NaN rows of invalid pairs.
+hipError_t launch_gemv(const GemvArgs& a, const GemvPlan& plan, void* partial, hipStream_t s, bool reduce = true);
+
+// Split outputs of a launch_gemv(..., reduce = false): valid pair p's row r
+// is, when its slot count splits * (pair_sub ? pair_sub[p] : 1) exceeds 1,
+// the sum over slots s in order, starting from 0.0f, of
+// partial[(s * n_pairs + p) * n + r]; otherwise y's own row.  partial is
+// NULL when the plan splits nothing.
+struct GemvPartials {
+  const float* partial;
+  int splits;
+  int max_slots;  // splits x the part cap: no pair has more slots
+  const int32_t* pair_sub;
+};
+GemvPartials gemv_partials(const GemvPlan& plan, void* partial);
 
 // h[p, c] = silu(gu[p, c]) * gu[p, d_ff + c], silu(v) = v / (1 + exp(-v)),
-// for gu [n_pairs, 2*d_ff] and h [n_pairs, d_ff] fp32 (d_ff a multiple of 4)
-hipError_t launch_swiglu(const float* gu, int64_t n_pairs, int64_t d_ff, float* h, hipStream_t s);
+// for gu [n_pairs, 2*d_ff] and h [n_pairs, d_ff] fp32 (d_ff a multiple of 4),
+// with gu the y of a launch_gemv(..., reduce = false) whose split rows are
+// added here (pair_expert / n_experts tell valid pairs)
+hipError_t launch_swiglu(const float* gu, const GemvPartials& parts, const int32_t* pair_expert, int64_t n_experts,
+                         int64_t n_pairs, int64_t d_ff, float* h, hipStream_t s);
 
-// y[t, :] = sum over k < top_k, in order, of w[t*top_k + k] * z[t*top_k + k, :]
-hipError_t launch_combine(const float* z, const float* w, int64_t n_tokens, int64_t top_k, int64_t n, float* y,
-                          hipStream_t s);
+// y[t, :] = sum over k < top_k, in order, of w[t*top_k + k] * z[t*top_k + k, :],
+// with z the y of a launch_gemv(..., reduce = false) over the pairs
+hipError_t launch_combine(const float* z, const GemvPartials& parts, const int32_t* pair_expert, int64_t n_experts,
+                          const float* w, int64_t n_tokens, int64_t top_k, int64_t n, float* y, hipStream_t s);
 
 struct GemmArgs {
   const uint8_t* w_table;
