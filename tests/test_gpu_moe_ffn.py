@@ -80,6 +80,24 @@ def test_shared_experts_and_invalid_pair(stq):
     _check(y, gu, dn, d_model, d_ff, xf, pe, pw, 2)
 
 
+@pytest.mark.parametrize("plan", ["2,2", "4,3", "1,4"])
+def test_split_outputs_added_by_the_elementwise_passes(stq, monkeypatch, plan):
+    """Both projections under forced (k splits, part cap) plans: the SwiGLU
+    and combine passes add the split slots themselves ("4,3": up to 12
+    slots, some parts empty), with shared experts (one routed to by every
+    token) and an invalid pair."""
+    monkeypatch.setenv("STQ_GEMV_PLAN", plan)
+    E, d_model, d_ff = 4, 1024, 1024
+    gu, dn, tg, td = _tables(31, E, d_model, d_ff)
+    n_tokens, top_k = 6, 3
+    pe = np.array([0, 1, 2, 0, 3, 1, 0, 2, 9, 0, 1, 3, 0, 2, 1, 0, 3, 2], dtype=np.int32)
+    pw = S.routing_weights(32, n_tokens, top_k)
+    xb, xf = S.bf16_normal(np.random.default_rng(33), (n_tokens, d_model))
+    y = _run(stq, (tg, td), E, d_model, d_ff, xb, pe, pw, top_k)
+    assert np.all(np.isnan(y[2])) and np.all(np.isfinite(np.delete(y, 2, axis=0)))
+    _check(y, gu, dn, d_model, d_ff, xf, pe, pw, top_k)
+
+
 def test_exact_hand_built_expert(stq):
     # gate rows (-1, 0, +1, +1 | others 0,+,+,+) d=1, up rows (+1, 0, +1, +1 | ...) d=2, down all (0,+,+,+) d=1:
     # with x = e_0, every output is 192 * 2 * silu(-1) up to fp32 rounding of the activation
