@@ -136,6 +136,22 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
                     int64_t n_tokens, const int32_t* pair_expert, const int32_t* pair_token,
                     int64_t n_pairs, float* y, stq_stream_t stream);
 
+/* The plan stq_gemv takes for these shapes (host only: no GPU work, and no
+ * GPU needed when n_cus > 0), so a caller can size the scratch arena before
+ * a capture or check a tuning override.  The three outputs are HOST
+ * pointers; all must be non-NULL (STQ_E_ARG otherwise).
+ *   n_experts, n, k, n_pairs  as for stq_gemv (same checks, same errors)
+ *   n_cus        compute units to plan for; 0 = the current device's (256
+ *                when no device answers)
+ *   splits       out: ranges the k blocks of a row are split into
+ *   max_parts    out: most k parts one split is cut into for an expert with
+ *                several tokens (an expert with m pairs takes min(m, max_parts))
+ *   scratch_bytes  out: scratch the call needs (0 when nothing is split)
+ * STQ_GEMV_PLAN is honoured as in stq_gemv.  n_pairs == 0 or n == 0 gives
+ * (1, 1, 0): stq_gemv launches nothing then. */
+stq_status stq_gemv_plan(int64_t n_experts, int64_t n, int64_t k, int64_t n_pairs, int32_t n_cus,
+                         int32_t* splits, int32_t* max_parts, int64_t* scratch_bytes);
+
 /* Routed-expert FFN of one MoE layer for a batch of decode tokens, its
  * expert projections in STQ1_0 (lemmy post 66506, paragraph "Runtime": the
  * routed experts' projections run through STQ1_0 kernels; routing top-k of

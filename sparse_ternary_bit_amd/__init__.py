@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "QK", "BLOCK_BYTES", "ENC_WLS", "ENC_AMAX", "StqError", "lib", "lib_path",
-    "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "grouped_gemm", "moe_ffn_decode",
+    "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "gemv_plan", "grouped_gemm", "moe_ffn_decode",
     "layer_errors", "q2_roundtrip", "greedy_allocation", "stream_read_probe",
 ]
 
@@ -66,6 +66,9 @@ def lib() -> ctypes.CDLL:
     L.stq_gemv.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_i64, _c_i64,
                            _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
     L.stq_gemv.restype = _c_int
+    L.stq_gemv_plan.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(_c_i64)]
+    L.stq_gemv_plan.restype = _c_int
     L.stq_grouped_gemm.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
     L.stq_grouped_gemm.restype = _c_int
     L.stq_moe_ffn_decode.argtypes = [_c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
@@ -140,6 +143,15 @@ def dequantize_rows(q: torch.Tensor, n: int, k: int, out: torch.Tensor | None = 
     _on_gpu("out", out, torch.float32)
     _check("stq_dequantize_rows", lib().stq_dequantize_rows(q.data_ptr(), n, k, out.data_ptr(), _stream()))
     return out
+
+
+def gemv_plan(n_experts: int, n: int, k: int, n_pairs: int, n_cus: int = 0) -> tuple[int, int, int]:
+    """(splits, max_parts, scratch_bytes) that gemv takes for these shapes on n_cus
+    compute units (0: the current device's); host only."""
+    sp, mp, sb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check("stq_gemv_plan", lib().stq_gemv_plan(int(n_experts), int(n), int(k), int(n_pairs), int(n_cus),
+                                                ctypes.byref(sp), ctypes.byref(mp), ctypes.byref(sb)))
+    return sp.value, mp.value, sb.value
 
 
 def gemv(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: int, k: int, x: torch.Tensor,

@@ -721,14 +721,14 @@ static void estimate_plan(const GemvArgs& a, int cus, int& best_splits, int& bes
 
 // The estimate depends only on the shapes and the CU count; decode loops
 // repeat a few shapes, so each host thread keeps its last 16 answers.
-GemvPlan plan_gemv(const GemvArgs& a) {
+GemvPlan plan_gemv(const GemvArgs& a, int for_cus) {
   struct Entry {
     int64_t n_pairs, n_experts, n, k;
     int cus, splits, bps, sub;
   };
   thread_local Entry cache[16];
   thread_local int cache_used = 0, cache_next = 0;
-  const int cus = device_cus();
+  const int cus = for_cus > 0 ? for_cus : device_cus();
   const int nb = static_cast<int>(a.k / kQK);
   const bool parts_ok = a.n_experts <= kLeadExperts;
   int best_splits = 0, best_bps = 0, best_sub = 0;

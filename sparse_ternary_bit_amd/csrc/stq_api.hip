@@ -157,6 +157,26 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
   return ok();
 }
 
+stq_status stq_gemv_plan(int64_t n_experts, int64_t n, int64_t k, int64_t n_pairs, int32_t n_cus,
+                         int32_t* splits, int32_t* max_parts, int64_t* scratch_bytes) {
+  if (!splits || !max_parts || !scratch_bytes) return fail(STQ_E_ARG, "stq_gemv_plan: null output pointer");
+  if (n_experts < 1 || n < 0 || n_pairs < 0 || n_cus < 0) return fail(STQ_E_ARG, "stq_gemv_plan: negative count or no experts");
+  if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "stq_gemv_plan: k=%lld is not a positive multiple of 256", (long long)k);
+  if (n > INT_MAX || n_experts > INT_MAX) return fail(STQ_E_SHAPE, "stq_gemv_plan: count exceeds int32");
+  if (n_pairs > 65535) return fail(STQ_E_SHAPE, "stq_gemv_plan: more than 65535 pairs in one call");
+  *splits = 1;
+  *max_parts = 1;
+  *scratch_bytes = 0;
+  if (n_pairs == 0 || n == 0) return ok();  // stq_gemv launches nothing
+  const stq::GemvArgs ga{nullptr, n * stq_row_bytes(k), n_experts, n, k, nullptr, 1, k, 1, nullptr, nullptr,
+                         n_pairs, nullptr, 1};
+  const stq::GemvPlan pl = stq::plan_gemv(ga, n_cus);
+  *splits = pl.splits;
+  *max_parts = pl.max_sub;
+  *scratch_bytes = pl.partial_bytes;
+  return ok();
+}
+
 stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_bytes, const uint8_t* w_down,
                               int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
                               const uint16_t* x, int64_t n_tokens, const int32_t* pair_expert,

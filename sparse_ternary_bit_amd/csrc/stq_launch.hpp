@@ -39,7 +39,8 @@ struct GemvPlan {
   int64_t partial_floats;
   int64_t partial_bytes;
 };
-GemvPlan plan_gemv(const GemvArgs& a);
+// cus: compute units the plan is made for (0: the current device's).
+GemvPlan plan_gemv(const GemvArgs& a, int cus = 0);
 // reduce = false leaves split outputs in `partial` for the caller to add (see
 // GemvPartials); the GEMV still writes y's rows that are not split and the
 // NaN rows of invalid pairs.

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for want in ("stq_quantize_rows", "stq_gemv", "stq_grouped_gemm", "stq_dequantize_rows",
                  "stq_moe_ffn_decode", "stq_layer_errors", "stq_q2_roundtrip", "stq_greedy_allocation",
-                 "stq_row_bytes", "stq_status_string", "stq_last_error"):
+                 "stq_gemv_plan", "stq_row_bytes", "stq_status_string", "stq_last_error"):
         assert want in names
 
 
@@ -104,6 +104,110 @@ def test_gemv_rejects_bad_arguments(L):
 def test_gemv_empty_work_is_ok_without_gpu(L):
     assert _gemv(L, np_=0, w=None, x=None, y=None) == 0
     assert _gemv(L, n=0, w=None, x=None, y=None) == 0
+
+
+def _plan(L, ne=256, n=4096, k=7168, np_=8, cus=256):
+    sp, mp, sb = ctypes.c_int32(-7), ctypes.c_int32(-7), ctypes.c_int64(-7)
+    st = L.stq_gemv_plan(ne, n, k, np_, cus, ctypes.byref(sp), ctypes.byref(mp), ctypes.byref(sb))
+    return st, (sp.value, mp.value, sb.value)
+
+
+def _scratch(splits, parts, n_pairs, n):
+    """Bytes of split outputs: fp32 partial sums per (slot, pair, row) padded
+    to 256 bytes, then one int per pair (its part count) when experts are
+    parted; nothing when no output is split."""
+    if splits * parts == 1:
+        return 0
+    return (splits * parts * n_pairs * n * 4 + 255) // 256 * 256 + (4 * n_pairs if parts > 1 else 0)
+
+
+def test_gemv_plan_for_the_decode_sweep(L, monkeypatch):
+    """The 256-expert 4096 x 7168 layer, top-8, on 256 CUs: the plans the
+    decode sweep runs under, and the scratch each needs."""
+    monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    for tokens, want in ((1, (7, 1)), (4, (2, 2)), (16, (1, 3)), (64, (1, 2))):
+        st, (sp, mp, sb) = _plan(L, np_=8 * tokens)
+        assert st == 0 and (sp, mp) == want, tokens
+        assert sb == _scratch(sp, mp, 8 * tokens, 4096)
+    assert _plan(L, np_=1) == (0, (28, 1, _scratch(28, 1, 1, 4096)))  # one pair: a block per workgroup
+    st, plan0 = _plan(L, cus=0)  # the current device's CUs, 256 when no device answers
+    assert st == 0
+    import torch
+    if not torch.cuda.is_available():
+        assert plan0 == _plan(L, cus=256)[1]
+
+
+def test_gemv_plan_fills_more_compute_units_with_more_splits(L, monkeypatch):
+    monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    splits = [_plan(L, np_=8, cus=c)[1][0] for c in (8, 64, 128, 256, 304, 512, 1024)]
+    assert splits == sorted(splits) and splits[0] < splits[-1]
+    for c in (8, 64, 128, 256, 304, 512, 1024):
+        for tokens in (1, 4, 16, 64):
+            st, (sp, mp, sb) = _plan(L, np_=8 * tokens, cus=c)
+            assert st == 0 and 1 <= sp <= 28 and 1 <= mp <= 8 and sb == _scratch(sp, mp, 8 * tokens, 4096)
+
+
+def test_gemv_plan_partial_sums_cap(L, monkeypatch):
+    """No plan writes more than 1 GiB of partial sums: from 4097 tokens of
+    top-8 on 4096 rows every output goes straight to y."""
+    monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    assert _plan(L, np_=8 * 4097) == (0, (1, 1, 0))
+    assert _plan(L, np_=65535) == (0, (1, 1, 0))
+    for np_ in (8, 100, 1000, 4000, 16384, 32768, 32776):
+        st, (sp, mp, sb) = _plan(L, np_=np_)
+        assert st == 0
+        assert (sp, mp) == (1, 1) or sp * mp * np_ * 4096 * 4 <= 2 ** 30
+
+
+@pytest.mark.parametrize("env,want", [("3,4", (3, 4)), ("5,8", (5, 8)), ("10,1", (10, 1)), ("27,1", (14, 1)),
+                                      ("28,2", (28, 2))])
+def test_gemv_plan_override(L, monkeypatch, env, want):
+    """STQ_GEMV_PLAN="s,p" replaces the estimate; s splits are rounded to the
+    split of ceil(28 / s) blocks each (27 -> 2 blocks -> 14 splits)."""
+    monkeypatch.setenv("STQ_GEMV_PLAN", env)
+    st, (sp, mp, sb) = _plan(L, np_=64)
+    assert st == 0 and (sp, mp) == want and sb == _scratch(sp, mp, 64, 4096)
+
+
+@pytest.mark.parametrize("env", ["0,1", "29,1", "3,9", "3,0", "x", "4", "-1,2"])
+def test_gemv_plan_ignores_malformed_overrides(L, monkeypatch, env):
+    monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    auto = _plan(L, np_=64)
+    monkeypatch.setenv("STQ_GEMV_PLAN", env)
+    assert _plan(L, np_=64) == auto
+
+
+def test_gemv_plan_parts_need_the_leader_table(L, monkeypatch):
+    """Experts are parted only while the workgroup's table space can rank
+    them (8208 experts); beyond, each expert is one unit even when forced."""
+    monkeypatch.setenv("STQ_GEMV_PLAN", "1,3")
+    assert _plan(L, ne=8208, np_=64)[1][:2] == (1, 3)
+    assert _plan(L, ne=8209, np_=64) == (0, (1, 1, 0))
+    monkeypatch.setenv("STQ_GEMV_PLAN", "4,3")
+    assert _plan(L, ne=9000, np_=64) == (0, (4, 1, _scratch(4, 1, 64, 4096)))
+
+
+def test_gemv_plan_rejects_bad_arguments(L):
+    assert _plan(L, k=1000)[0] == 2
+    assert _plan(L, ne=0)[0] == 1
+    assert _plan(L, np_=70000)[0] == 2
+    assert _plan(L, np_=-1)[0] == 1
+    assert _plan(L, n=-1)[0] == 1
+    assert _plan(L, cus=-1)[0] == 1
+    sp, mp = ctypes.c_int32(), ctypes.c_int32()
+    assert L.stq_gemv_plan(256, 4096, 7168, 8, 256, ctypes.byref(sp), ctypes.byref(mp), None) == 1
+    assert "null" in _err(L)
+    # nothing to launch: no split, no scratch
+    assert _plan(L, np_=0) == (0, (1, 1, 0))
+    assert _plan(L, n=0) == (0, (1, 1, 0))
+
+
+def test_gemv_plan_binding(monkeypatch):
+    import sparse_ternary_bit_amd as stq
+    monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    assert stq.gemv_plan(256, 4096, 7168, 128, n_cus=256) == (1, 3, _scratch(1, 3, 128, 4096))
+    with pytest.raises(stq.StqError):
+        stq.gemv_plan(256, 4096, 1000, 8)
 
 
 def test_grouped_gemm_rejects_bad_arguments(L):

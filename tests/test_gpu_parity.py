@@ -225,6 +225,15 @@ def test_gemv_wide_batch(stq):
                     GEMV_TOL, f"pair {i}")
 
 
+def test_gemv_plan_uses_the_device_cu_count(stq, monkeypatch):
+    """stq_gemv_plan with n_cus = 0 plans for the current device's compute
+    units, as stq_gemv does."""
+    monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for n_pairs in (1, 8, 32, 128, 512):
+        assert stq.gemv_plan(256, 4096, 7168, n_pairs) == stq.gemv_plan(256, 4096, 7168, n_pairs, n_cus=cus)
+
+
 @pytest.mark.parametrize("plan", [None, "1,2", "1,8", "2,3", "3,4", "5,8", "10,1"])
 def test_gemv_token_parts_match_oracle(stq, monkeypatch, plan):
     """Experts with 0-8 tokens under forced (k splits, part cap) plans: an
