@@ -27,10 +27,11 @@
 //     k-quarter: for each of
 //     the block's 8 k-steps the quarter's two group codes, pre-scaled by 4 so
 //     a code is directly a byte offset into the pattern table;
-//   * per pair of k-steps the MFMA lanes read one record word; per k-step a
-//     lane extracts two codes (two bit-field extracts) and reads the bf16 lanes of
-//     both patterns from a 32-entry table in LDS (two 8-byte reads): that is
-//     the whole weight decode;
+//   * per k-step an MFMA lane reads its four row tiles' record words (one
+//     16-byte read; a word serves two k-steps), and per row tile extracts
+//     two codes (two bit-field extracts) and reads the bf16 lanes of both
+//     patterns from a 32-entry table in LDS (two 8-byte reads): that is the
+//     whole weight decode;
 //   * after the block's 8 k-steps the fp32 partial sums are scaled by the
 //     rows' d into the fp32 totals.
 // One barrier per block.  Workgroups of one expert are launched on the same
@@ -77,10 +78,11 @@ struct Smem {
   uint32_t lut[64];
   float dsc[kWaves][kTileRows];           // fp32(d) of each row's current block
   // records: word s2 (k-steps 2*s2, 2*s2+1) of quarter q of row r of row tile
-  // i sits at rec[wave][s2][q][i ^ q][r]; both the writers (a row tile's 16
-  // rows per half wave) and the readers (two quarters per half wave) then
-  // touch 32 distinct banks
-  uint32_t rec[kWaves][4][4][4][16];
+  // i sits at rec[wave][s2][q][r][i], so an MFMA lane's four row-tile words
+  // are one 16-byte read and a wavefront reads 1 KB in one contiguous run
+  // (the writers, a row tile per 16 lanes, meet 2-way bank conflicts on
+  // their 4-byte stores, which cost less than the 4-byte reads they replace)
+  alignas(16) uint32_t rec[kWaves][4][4][16][4];
   alignas(16) char x[2][kXBuf];           // activations, current and next block
   alignas(16) char wraw[kWaves][kWRaw];   // each wavefront's tile run of the next block
 };
@@ -163,10 +165,10 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
     const int ti = lane >> 4, tr = lane & 15;
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
-      sh.rec[wave][s2][0][ti ^ 0][tr] = __builtin_amdgcn_perm(cl[2 * s2 + 1], cl[2 * s2], 0x05040100u);
-      sh.rec[wave][s2][1][ti ^ 1][tr] = __builtin_amdgcn_perm(cl[2 * s2 + 1], cl[2 * s2], 0x07060302u);
-      sh.rec[wave][s2][2][ti ^ 2][tr] = __builtin_amdgcn_perm(cu[2 * s2 + 1], cu[2 * s2], 0x05040100u);
-      sh.rec[wave][s2][3][ti ^ 3][tr] = __builtin_amdgcn_perm(cu[2 * s2 + 1], cu[2 * s2], 0x07060302u);
+      sh.rec[wave][s2][0][tr][ti] = __builtin_amdgcn_perm(cl[2 * s2 + 1], cl[2 * s2], 0x05040100u);
+      sh.rec[wave][s2][1][tr][ti] = __builtin_amdgcn_perm(cl[2 * s2 + 1], cl[2 * s2], 0x07060302u);
+      sh.rec[wave][s2][2][tr][ti] = __builtin_amdgcn_perm(cu[2 * s2 + 1], cu[2 * s2], 0x05040100u);
+      sh.rec[wave][s2][3][tr][ti] = __builtin_amdgcn_perm(cu[2 * s2 + 1], cu[2 * s2], 0x07060302u);
     }
     sh.dsc[wave][lane] = half_bits_to_float(blk.d16);
   };
@@ -207,9 +209,7 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       bf16x8_t A[4];
-      uint32_t Rw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Rw[i] = sh.rec[wave][s >> 1][q][i ^ q][r];
+      const u32x4_t Rw = *reinterpret_cast<const u32x4_t*>(&sh.rec[wave][s >> 1][q][r][0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t w = Rw[i];
