@@ -189,7 +189,11 @@ stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_b
  *   y               [total_m, n] fp32: y[r, :] = W_e x_sorted[r, :]
  * bf16 x ternary products on matrix cores (exact), fp32 accumulation, one
  * fp32 multiply by d per 256-weight block.  Offsets that break the stated
- * invariants are outside the contract (rows may be skipped). */
+ * invariants are outside the contract, but the kernel clamps each expert's
+ * rows to [0, total_m] (lo = clamp(offsets[e]), hi = clamp(offsets[e+1])
+ * and at least lo), so x_sorted and y are never accessed outside their
+ * total_m rows: rows in no range are left unwritten and rows in two ranges
+ * get either expert's result. */
 stq_status stq_grouped_gemm(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts,
                             int64_t n, int64_t k, const uint16_t* x_sorted,
                             const int32_t* expert_offsets, int64_t total_m, float* y,

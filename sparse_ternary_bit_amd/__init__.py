@@ -108,6 +108,18 @@ def _on_gpu(name: str, t: torch.Tensor, dtype: torch.dtype) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _holds(name: str, t: torch.Tensor, n: int) -> None:
+    """The kernels index raw pointers: a buffer smaller than the shapes say would be read or
+    written past its end, so it is refused here."""
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
+def _table(name: str, t: torch.Tensor, n_experts: int, stride: int, n: int, k: int) -> None:
+    if n_experts > 0 and n > 0:
+        _holds(name, t, (int(n_experts) - 1) * int(stride) + int(n) * row_bytes(k))
+
+
 def row_bytes(k: int) -> int:
     rb = lib().stq_row_bytes(int(k))
     if rb < 0:
@@ -123,6 +135,7 @@ def quantize_rows(w: torch.Tensor, imatrix: torch.Tensor | None = None, encoder:
     n, k = w.shape
     if imatrix is not None:
         _on_gpu("imatrix", imatrix, torch.float32)
+        _holds("imatrix", imatrix, k)
     if out is None:
         out = torch.empty(n * row_bytes(k), dtype=torch.uint8, device=w.device)
     _on_gpu("out", out, torch.uint8)
@@ -141,6 +154,7 @@ def dequantize_rows(q: torch.Tensor, n: int, k: int, out: torch.Tensor | None = 
     if out is None:
         out = torch.empty((n, k), dtype=torch.float32, device=q.device)
     _on_gpu("out", out, torch.float32)
+    _holds("out", out, n * k)
     _check("stq_dequantize_rows", lib().stq_dequantize_rows(q.data_ptr(), n, k, out.data_ptr(), _stream()))
     return out
 
@@ -182,6 +196,9 @@ def gemv(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: int, k: i
     if out is None:
         out = torch.empty((n_pairs, n), dtype=torch.float32, device=x.device)
     _on_gpu("out", out, torch.float32)
+    _holds("out", out, int(n_pairs) * int(n))
+    if int(n_pairs) > 0:
+        _table("w_table", w_table, n_experts, expert_stride, n, k)
     # a one-row view may carry any stride in its first dimension; its rows are k apart
     x_stride = x.stride(0) if n_tokens > 1 else x.shape[1]
     _check("stq_gemv", lib().stq_gemv(w_table.data_ptr(), int(expert_stride), int(n_experts), int(n), int(k),
@@ -198,10 +215,15 @@ def grouped_gemm(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: i
     _on_gpu("offsets", offsets, torch.int32)
     if offsets.numel() != n_experts + 1:
         raise ValueError("offsets must hold n_experts + 1 entries")
+    if x_sorted.dim() != 2 or x_sorted.shape[1] != k:
+        raise ValueError("x_sorted must be [total_m, k]")
     total_m = x_sorted.shape[0]
     if out is None:
         out = torch.empty((total_m, n), dtype=torch.float32, device=x_sorted.device)
     _on_gpu("out", out, torch.float32)
+    _holds("out", out, total_m * int(n))
+    if total_m > 0:
+        _table("w_table", w_table, n_experts, expert_stride, n, k)
     _check("stq_grouped_gemm", lib().stq_grouped_gemm(w_table.data_ptr(), int(expert_stride), int(n_experts),
                                                       int(n), int(k), x_sorted.data_ptr(), offsets.data_ptr(),
                                                       total_m, out.data_ptr(), _stream()))
@@ -218,14 +240,18 @@ def moe_ffn_decode(w_gate_up: torch.Tensor, gate_up_stride: int, w_down: torch.T
     _on_gpu("x", x, torch.bfloat16)
     _on_gpu("pair_expert", pair_expert, torch.int32)
     _on_gpu("pair_weight", pair_weight, torch.float32)
-    n_tokens = x.shape[0]
-    if x.shape[1] != d_model:
+    if x.dim() != 2 or x.shape[1] != d_model:
         raise ValueError("x must be [n_tokens, d_model]")
+    n_tokens = x.shape[0]
     if pair_expert.numel() != n_tokens * top_k or pair_weight.numel() != n_tokens * top_k:
         raise ValueError("pair_expert and pair_weight must hold n_tokens*top_k entries")
     if out is None:
         out = torch.empty((n_tokens, d_model), dtype=torch.float32, device=x.device)
     _on_gpu("out", out, torch.float32)
+    _holds("out", out, n_tokens * int(d_model))
+    if n_tokens > 0:
+        _table("w_gate_up", w_gate_up, n_experts, gate_up_stride, 2 * int(d_ff), d_model)
+        _table("w_down", w_down, n_experts, down_stride, d_model, d_ff)
     _check("stq_moe_ffn_decode",
            lib().stq_moe_ffn_decode(w_gate_up.data_ptr(), int(gate_up_stride), w_down.data_ptr(), int(down_stride),
                                     int(n_experts), int(d_model), int(d_ff), x.data_ptr(), n_tokens,

@@ -66,6 +66,7 @@ struct GArgs {
   int64_t k;
   const uint16_t* x;
   const int32_t* offsets;
+  int64_t total_m;
   float* y;
   int nslab;
   int vec4;  // n % 4 == 0: outputs stored 16 bytes at a time
@@ -280,8 +281,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GArgs a) {
   const int slab = local % a.nslab;
   const int e = (local / a.nslab) * kXcds + xcd;
   if (e >= a.n_experts) return;
-  const int m0 = a.offsets[e];
-  const int m = a.offsets[e + 1] - m0;
+  // the expert's rows, clamped to [0, total_m] so that offsets outside the
+  // contract can neither read past x_sorted nor write past y
+  const int64_t lo = min(max(static_cast<int64_t>(a.offsets[e]), int64_t{0}), a.total_m);
+  const int64_t hi = min(max(static_cast<int64_t>(a.offsets[e + 1]), lo), a.total_m);
+  const int m0 = static_cast<int>(lo);
+  const int m = static_cast<int>(hi - lo);
   if (m <= 0) return;
 
   if (threadIdx.x < 32) {
@@ -325,6 +330,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& ga, hipStream_t s) {
   a.k = ga.k;
   a.x = ga.x;
   a.offsets = ga.offsets;
+  a.total_m = ga.total_m;
   a.y = ga.y;
   a.nslab = static_cast<int>((ga.n + kSlab - 1) / kSlab);
   a.vec4 = (ga.n % 4) == 0;

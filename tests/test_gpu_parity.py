@@ -451,6 +451,70 @@ def test_grouped_gemm_empty_and_single_rows(stq):
     assert np.all(np.abs(gv - y[0]) <= 2 * GEMM_TOL * A)
 
 
+def test_grouped_gemm_offsets_outside_the_contract_stay_in_bounds(stq):
+    """Offsets that are negative, decreasing or past total_m: each expert's
+    rows are clamped to [0, total_m], so nothing is read past x_sorted and
+    sentinel rows after y stay untouched; rows in one range match that
+    expert, rows in two ranges match one of them."""
+    k, n, total_m = 512, 96, 12
+    offsets = np.array([-5, 4, 2, 50], dtype=np.int32)
+    # clamped: expert 0 [0, 4); expert 1 lo = 4, hi = max(2, 4) = 4 (empty); expert 2 [2, 12)
+    ranges = [(0, 4), (4, 4), (2, 12)]
+    table, stride = _grouped_case(k, n, np.array([0, 1, 1, 1], dtype=np.int32), 950)
+    xb, xf = S.bf16_normal(np.random.default_rng(11), (total_m, k))
+    big = torch.full((total_m + 3, n), 7.0, dtype=torch.float32, device="cuda")
+    out = big[:total_m]
+    stq.grouped_gemm(dev(table), stride, 3, n, k, dev(xb.view(np.int16)).view(torch.bfloat16), dev(offsets),
+                     out=out)
+    yb = host(big)
+    assert np.all(yb[total_m:] == 7.0)
+    rb = O.row_bytes(k)
+    refs = []
+    for e in range(3):
+        raw = table[e * stride: e * stride + n * rb]
+        refs.append((O.gemv_tokens(raw, n, k, xf), O.tolerance_scale(raw, n, k, xf)))
+    for r in range(total_m):
+        owners = [e for e, (lo, hi) in enumerate(ranges) if lo <= r < hi]
+        assert owners, r
+        ok = [np.all(np.abs(yb[r] - refs[e][0][r]) <= GEMM_TOL * refs[e][1][r]) for e in owners]
+        assert any(ok), (r, owners)
+
+
+def test_binding_refuses_buffers_smaller_than_the_shapes(stq):
+    """The binding checks every buffer the kernels index against the shapes
+    before any launch: outputs, weight tables, activation rows, importance."""
+    k, n, E = 256, 64, 3
+    rb = O.row_bytes(k)
+    table = torch.zeros(E * n * rb, dtype=torch.uint8, device="cuda")
+    short = table[: (E - 1) * n * rb + n * rb - 1]
+    x = torch.zeros((2, k), dtype=torch.bfloat16, device="cuda")
+    pe = torch.zeros(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="out"):
+        stq.gemv(table, n * rb, E, n, k, x, pe, out=torch.empty((1, n), device="cuda"))
+    with pytest.raises(ValueError, match="w_table"):
+        stq.gemv(short, n * rb, E, n, k, x, pe)
+    offs = torch.tensor([0, 1, 2, 2], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="out"):
+        stq.grouped_gemm(table, n * rb, E, n, k, x, offs, out=torch.empty((2, n - 1), device="cuda"))
+    with pytest.raises(ValueError, match="w_table"):
+        stq.grouped_gemm(short, n * rb, E, n, k, x, offs)
+    with pytest.raises(ValueError, match="x_sorted"):
+        stq.grouped_gemm(table, n * rb, E, n, k, torch.zeros((2, 2 * k), dtype=torch.bfloat16, device="cuda"), offs)
+    with pytest.raises(ValueError, match="out"):
+        stq.dequantize_rows(table, n, k, out=torch.empty((n, k - 1), device="cuda"))
+    with pytest.raises(ValueError, match="imatrix"):
+        stq.quantize_rows(torch.zeros((4, k), device="cuda"), torch.ones(k - 1, device="cuda"))
+    d_model, d_ff = 256, 256
+    tg = torch.zeros(E * 2 * d_ff * O.row_bytes(d_model), dtype=torch.uint8, device="cuda")
+    td = torch.zeros(E * d_model * O.row_bytes(d_ff), dtype=torch.uint8, device="cuda")
+    pw = torch.ones(2, dtype=torch.float32, device="cuda")
+    sg, sd = 2 * d_ff * O.row_bytes(d_model), d_model * O.row_bytes(d_ff)
+    with pytest.raises(ValueError, match="out"):
+        stq.moe_ffn_decode(tg, sg, td, sd, E, d_model, d_ff, x, pe, pw, 1, out=torch.empty((1, d_model), device="cuda"))
+    with pytest.raises(ValueError, match="w_down"):
+        stq.moe_ffn_decode(tg, sg, td[:-1], sd, E, d_model, d_ff, x, pe, pw, 1)
+
+
 def test_stream_read_probe_runs(stq):
     """The read-rate reference kernel (measurement only) over a small and a
     ragged buffer: it completes and leaves the buffer untouched."""
