@@ -94,9 +94,9 @@ int64_t stq_row_bytes(int64_t k);
  *   out      packed matrix, n_rows*k/256*42 bytes (layout above)
  * Sums run in fp64 in a fixed order (lanes of a group in order, then a
  * balanced tree of adjacent groups); d is stored as fp16 via fp32
- * (round-to-nearest-even both times, clamped to 65504).  The result is
- * bit-identical to the reference encoder.  Non-finite inputs are outside
- * the contract (output unspecified). */
+ * (round-to-nearest-even both times, clamped to 65504).  These rules fix
+ * every output byte: any implementation that follows them gives the same
+ * bytes.  Non-finite inputs are outside the contract (output unspecified). */
 stq_status stq_quantize_rows(const float* w, const float* imatrix, int64_t n_rows, int64_t k,
                              int encoder, int rounds, uint8_t* out, stq_stream_t stream);
 
@@ -232,8 +232,8 @@ stq_status stq_layer_errors(const float* w, const float* w_hat, int64_t n_rows, 
  * sqrt(ss/256)/2 (fp64 -> fp32 -> fp16, round-to-nearest-even, clamped to
  * 65504); each weight becomes s if |w| < 2s, else 3s, with the sign bit of w.
  *   w, out  [n_rows, k] fp32, row-major, 16-byte aligned (may not overlap)
- * Bit-identical to the reference definition.  Non-finite inputs give
- * unspecified (non-finite) outputs for their block. */
+ * These rules fix every output bit.  Non-finite inputs give unspecified
+ * (non-finite) outputs for their block. */
 stq_status stq_q2_roundtrip(const float* w, int64_t n_rows, int64_t k, float* out, stq_stream_t stream);
 
 /* Greedy per-byte allocation of the larger format over layers (lemmy post
