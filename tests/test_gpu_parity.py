@@ -515,6 +515,28 @@ def test_binding_refuses_buffers_smaller_than_the_shapes(stq):
         stq.moe_ffn_decode(tg, sg, td[:-1], sd, E, d_model, d_ff, x, pe, pw, 1)
 
 
+def test_empty_calls_succeed_without_work(stq):
+    """Zero pairs, zero decode tokens, zero prefill rows and zero rows to
+    encode: every entry point returns an empty result without error."""
+    k, n, E = 256, 64, 2
+    rb = O.row_bytes(k)
+    table = torch.zeros(E * n * rb, dtype=torch.uint8, device="cuda")
+    x0 = torch.zeros((0, k), dtype=torch.bfloat16, device="cuda")
+    pe0 = torch.zeros(0, dtype=torch.int32, device="cuda")
+    assert tuple(stq.gemv(table, n * rb, E, n, k, x0, pe0).shape) == (0, n)
+    offs = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    assert tuple(stq.grouped_gemm(table, n * rb, E, n, k, x0, offs).shape) == (0, n)
+    assert stq.quantize_rows(torch.zeros((0, k), device="cuda")).numel() == 0
+    assert tuple(stq.dequantize_rows(table, 0, k).shape) == (0, k)
+    d_model = d_ff = 256
+    tg = torch.zeros(E * 2 * d_ff * O.row_bytes(d_model), dtype=torch.uint8, device="cuda")
+    td = torch.zeros(E * d_model * O.row_bytes(d_ff), dtype=torch.uint8, device="cuda")
+    y = stq.moe_ffn_decode(tg, 2 * d_ff * O.row_bytes(d_model), td, d_model * O.row_bytes(d_ff), E, d_model, d_ff,
+                           x0, pe0, torch.zeros(0, dtype=torch.float32, device="cuda"), 2)
+    assert tuple(y.shape) == (0, d_model)
+    torch.cuda.synchronize()
+
+
 def test_stream_read_probe_runs(stq):
     """The read-rate reference kernel (measurement only) over a small and a
     ragged buffer: it completes and leaves the buffer untouched."""
