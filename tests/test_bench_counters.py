@@ -6,8 +6,6 @@ import csv
 import json
 import os
 
-import pytest
-
 import bench
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
