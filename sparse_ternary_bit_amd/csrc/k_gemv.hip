@@ -18,10 +18,10 @@
 // code (already scaled by 4) and, per token, one LDS read with the group's
 // table offset as an immediate plus one fp32 add; the block's fp16 scale
 // multiplies the block sum.  All threads of a wavefront read the same group's
-// 128-byte table at once, so the reads are bank-conflict free.  With bf16
-// activations and 2-4 tokens in a pass, two tokens share an 8-byte table
-// entry and one 8-byte read serves both (an LDS read issues at the same rate
-// for 4 and 8 bytes, and the table reads bound the extra tokens of a pass).
+// 128-byte table at once, so the reads are bank-conflict free.  With 2-4
+// tokens in a pass, two tokens share an 8-byte table entry and one 8-byte
+// read serves both (an LDS read issues at the same rate for 4 and 8 bytes,
+// and the table reads bound the extra tokens of a pass).
 // Tables are double-buffered: while block b is summed from one buffer, block
 // b+1's table is built into the other, one barrier per block.
 //
@@ -60,8 +60,7 @@ constexpr int kMT = 4;                     // tokens per pass
 constexpr int kTabBytes = kGroups * 32 * 4;
 constexpr int kTokStride = kTabBytes + 16; // token tables apart by a non-multiple of 256 bytes
 constexpr int kBufBytes = kMT * kTokStride;
-// With bf16 activations, passes of 2 or more tokens tabulate two tokens to
-// an 8-byte entry: group g's 256-byte table at g * 256, the second pair's
+// Passes of 2 or more tokens tabulate two tokens to an 8-byte entry: group g's 256-byte table at g * 256, the second pair's
 // tables kPairStride further (16-byte aligned and not a multiple of 512, so
 // the compiler keeps the two pairs' reads apart instead of fusing them into
 // one 16-byte read that it then waits on read by read).
@@ -311,10 +310,10 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // Table items of this thread.  Pair tables (bf16 activations, MC = 2 or 4):
+  // Table items of this thread.  Pair tables (MC = 2 or 4):
   // item (token pair tid / 256, group g, zero lane z), one per thread.  Else
   // item i = 256*m + 4*g + z for token m, items tid and tid + 512.
-  constexpr bool kPair = kMode == kXBF16 && MC >= 2;
+  constexpr bool kPair = MC >= 2;
   static_assert(!kPair || MC == 2 || MC == 4, "pair tables take 2 or 4 tokens");
   constexpr int kItems = kPair ? 128 * MC : 256 * MC;
   const int it_g = (tid >> 2) & 63, it_z = tid & 3;
@@ -550,8 +549,7 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
       case 1: run_chunk<kMode, 1>(a, sh, wexp, b_begin, b_end, acc); break;
       case 2: run_chunk<kMode, 2>(a, sh, wexp, b_begin, b_end, acc); break;
       case 3:  // pair tables take 3 tokens as 4 (the fourth repeats the third, its sums unused)
-        if constexpr (kMode == kXBF16) run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc);
-        else run_chunk<kMode, 3>(a, sh, wexp, b_begin, b_end, acc);
+        run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc);
         break;
       default: run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc); break;
     }
@@ -571,8 +569,11 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
   }
 }
 
+// At most 128 VGPRs (4 waves per SIMD, two workgroups per CU as the LDS
+// allows); the fp32-row kernel's pair-table builds need a few bytes of
+// spill outside the block loop to stay there.
 template <int kMode>
-__global__ __launch_bounds__(kRows) void gemv_kernel(KArgs a) {
+__global__ __launch_bounds__(kRows, 4) void gemv_kernel(KArgs a) {
   gemv_main<kMode>(a);
 }
 
