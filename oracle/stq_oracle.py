@@ -454,26 +454,29 @@ def silu(v: np.ndarray) -> np.ndarray:
     return out
 
 
-def _ffn_pair(gate_up: np.ndarray, down: np.ndarray, d_model: int, d_ff: int, x: np.ndarray):
-    """g, u, h, z of one (token, expert) pair, all fp64."""
+def _ffn_pair(gate_up: np.ndarray, down: np.ndarray, d_model: int, d_ff: int, x: np.ndarray, n_out: int):
+    """g, u, h, z of one (token, expert) pair, all fp64 (z: the n_out rows `down` holds)."""
     gu = gemv(gate_up, 2 * d_ff, d_model, x)
     g, u = gu[:d_ff], gu[d_ff:]
     h = silu(g) * u
-    z = gemv(down, d_model, d_ff, h)
+    z = gemv(down, n_out, d_ff, h)
     return g, u, h, z
 
 
 def moe_ffn_decode(gate_up: dict, down: dict, d_model: int, d_ff: int, x: np.ndarray,
-                   pair_expert: np.ndarray, pair_weight: np.ndarray, top_k: int) -> np.ndarray:
+                   pair_expert: np.ndarray, pair_weight: np.ndarray, top_k: int, n_out: int | None = None) -> np.ndarray:
     """y[t] = sum_k w[t*top_k + k] * W_down_e (silu(W_gate_e x_t) * (W_up_e x_t)), fp64.
 
     gate_up[e] / down[e]: packed matrices of expert e ([2*d_ff, d_model] and
-    [d_model, d_ff]); a pair whose expert is not among them makes its token's
-    row NaN."""
+    [n_out, d_ff]: n_out rows of the down projection, all d_model of them by
+    default; rows of a matrix-vector product are independent, so a subset of
+    rows gives the same outputs for those rows); a pair whose expert is not
+    among them makes its token's row NaN."""
+    n_out = d_model if n_out is None else int(n_out)
     x = np.asarray(x, dtype=np.float64).reshape(-1, d_model)
     pe = np.asarray(pair_expert).reshape(-1)
     pw = np.asarray(pair_weight, dtype=np.float64).reshape(-1)
-    y = np.zeros((x.shape[0], d_model), dtype=np.float64)
+    y = np.zeros((x.shape[0], n_out), dtype=np.float64)
     for t in range(x.shape[0]):
         for k in range(top_k):
             p = t * top_k + k
@@ -481,40 +484,43 @@ def moe_ffn_decode(gate_up: dict, down: dict, d_model: int, d_ff: int, x: np.nda
             if e not in gate_up or e not in down:
                 y[t] = np.nan
                 continue
-            y[t] = y[t] + pw[p] * _ffn_pair(gate_up[e], down[e], d_model, d_ff, x[t])[3]
+            y[t] = y[t] + pw[p] * _ffn_pair(gate_up[e], down[e], d_model, d_ff, x[t], n_out)[3]
     return y
 
 
 def moe_ffn_tolerance(gate_up: dict, down: dict, d_model: int, d_ff: int, x: np.ndarray,
                       pair_expert: np.ndarray, pair_weight: np.ndarray, top_k: int,
-                      tol: float = 1e-3, eps_act: float = 1e-6, eps_sum: float = 2.0 ** -23) -> np.ndarray:
+                      tol: float = 1e-3, eps_act: float = 1e-6, eps_sum: float = 2.0 ** -23,
+                      n_out: int | None = None) -> np.ndarray:
     """Per-element bound on |y_gpu - y| derived from the GEMV bound |err| <= tol * A.
 
     For a pair with exact g, u, h (fp64) and GEMV bounds dg = tol*A_g, du = tol*A_u:
       |dh| <= L*dg*(|u| + du) + |silu(g)|*du + eps_act*(|h| + ...)      (L = max|silu'|)
       |dz| <= |W_down| dh + tol * A_down(|h| + dh)
     and the fp32 combine adds at most top_k*eps_sum*sum_k |w_k| (|z_k| + dz_k):
-      bound[t] = sum_k |w_k| dz_k + top_k*eps_sum*sum_k |w_k| (|z_k| + dz_k)."""
+      bound[t] = sum_k |w_k| dz_k + top_k*eps_sum*sum_k |w_k| (|z_k| + dz_k).
+    n_out: rows held by each down matrix, as in moe_ffn_decode."""
+    n_out = d_model if n_out is None else int(n_out)
     x = np.asarray(x, dtype=np.float64).reshape(-1, d_model)
     pe = np.asarray(pair_expert).reshape(-1)
     pw = np.abs(np.asarray(pair_weight, dtype=np.float64).reshape(-1))
-    bound = np.zeros((x.shape[0], d_model), dtype=np.float64)
+    bound = np.zeros((x.shape[0], n_out), dtype=np.float64)
     for t in range(x.shape[0]):
-        acc_dz = np.zeros(d_model)
-        acc_mag = np.zeros(d_model)
+        acc_dz = np.zeros(n_out)
+        acc_mag = np.zeros(n_out)
         for k in range(top_k):
             p = t * top_k + k
             e = int(pe[p])
             if e not in gate_up or e not in down:
                 bound[t] = np.nan
                 break
-            g, u, h, z = _ffn_pair(gate_up[e], down[e], d_model, d_ff, x[t])
+            g, u, h, z = _ffn_pair(gate_up[e], down[e], d_model, d_ff, x[t], n_out)
             a_gu = tolerance_scale(gate_up[e], 2 * d_ff, d_model, x[t])[0]
             dg, du = tol * a_gu[:d_ff], tol * a_gu[d_ff:]
             dh = SILU_LIPSCHITZ * dg * (np.abs(u) + du) + np.abs(silu(g)) * du
             dh = dh + eps_act * (np.abs(h) + dh)
-            w_abs = np.abs(dequantize_rows(down[e], d_model, d_ff).astype(np.float64))
-            dz = w_abs @ dh + tol * tolerance_scale(down[e], d_model, d_ff, np.abs(h) + dh)[0]
+            w_abs = np.abs(dequantize_rows(down[e], n_out, d_ff).astype(np.float64))
+            dz = w_abs @ dh + tol * tolerance_scale(down[e], n_out, d_ff, np.abs(h) + dh)[0]
             acc_dz += pw[p] * dz
             acc_mag += pw[p] * (np.abs(z) + dz)
         else:

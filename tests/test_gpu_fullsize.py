@@ -106,26 +106,28 @@ def test_moe_decode_step(W, table, n_tokens, seed):
 
 
 def test_prefill_grouped_gemm(W, table):
+    """The 2048-token prefill: six experts' outputs (every row routed to each,
+    14 sampled columns) against the oracle.  The oracle's activation rows are
+    the unsorted draw indexed by the routing (host side), not the permuted
+    copy the kernel read, so a wrong permutation fails here; each expert is
+    checked elementwise and normwise on its own."""
     import sparse_ternary_bit_amd as stq
     t, stride, q = table
     x_sorted, offsets_t, row_token, offsets = W.prefill_batch()
     assert offsets[-1] == 16384 and int(np.max(np.diff(offsets))) > 64
     y = stq.grouped_gemm(t, stride, W.N_EXPERTS, N, K, x_sorted, offsets_t)
     torch.cuda.synchronize()
+    x = S.torch_bf16_normal(8, (2048, K)).float().cpu().numpy()   # the draw prefill_batch routes
     rng = np.random.default_rng(2)
-    sample_rows = np.unique(np.concatenate([[0, 16383], rng.integers(0, 16384, 40)]))
-    cols = np.unique(np.concatenate([[0, 4095], rng.integers(0, N, 10)]))
-    xs = x_sorted.index_select(0, torch.as_tensor(sample_rows, device="cuda")).float().cpu().numpy()
-    ys = y.index_select(0, torch.as_tensor(sample_rows, device="cuda")).cpu().numpy()[:, cols]
-    experts = np.searchsorted(offsets, sample_rows, side="right") - 1
-    worst_abs, worst_ref = 0.0, 0.0
-    for e in np.unique(experts):
+    cols = np.unique(np.concatenate([[0, 4095], rng.integers(0, N, 12)]))
+    experts = np.unique(np.concatenate([[0, 255, int(np.argmax(np.diff(offsets)))], rng.integers(1, 255, 3)]))
+    for e in experts:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        xs = x[row_token[lo:hi]]
+        ys = y[lo:hi].cpu().numpy()[:, cols].astype(np.float64)
         raw = _oracle_rows(W, int(e), cols, q)
-        sel = experts == e
-        y_ref = O.gemv_tokens(raw, len(cols), K, xs[sel])
-        A = O.tolerance_scale(raw, len(cols), K, xs[sel])
-        err = np.abs(ys[sel].astype(np.float64) - y_ref)
+        y_ref = O.gemv_tokens(raw, len(cols), K, xs)
+        A = O.tolerance_scale(raw, len(cols), K, xs)
+        err = np.abs(ys - y_ref)
         assert np.all(err <= GEMM_TOL * A), (int(e), float(np.max(err / A)))
-        worst_abs = max(worst_abs, float(np.max(err)))
-        worst_ref = max(worst_ref, float(np.max(np.abs(y_ref))))
-    assert worst_abs <= GEMM_TOL * worst_ref
+        assert np.max(err) <= GEMM_TOL * np.max(np.abs(y_ref)), int(e)

@@ -122,31 +122,77 @@ def test_exact_hand_built_expert(stq):
     assert np.all(np.abs(y - expect) <= 1e-5 * abs(expect))
 
 
-def test_full_size_token_matches_oracle(stq):
-    """d_model 7168, d_ff 2048, 256-expert tables encoded on the GPU; one bf16
-    token routed to 3 experts: the oracle encodes those experts' raw fp32
-    draws itself and computes all 7168 outputs."""
+@pytest.fixture(scope="module")
+def full_tables(stq):
+    """The benchmark's layer: 256 experts, gate/up 4096 x 7168 and down
+    7168 x 2048 in STQ1_0, encoded on the GPU from the seeded fp32 draws."""
     import stq_workloads as W
     q = W.table_imatrix()
     tg, sg = W.encode_table(imatrix=q)
     td, sd = W.encode_down_table()
+    torch.cuda.synchronize()
+    return (tg, sg), (td, sd), q.cpu().numpy()
+
+
+def _oracle_layer(experts, qn, down_rows):
+    """The oracle's own encodings of the listed experts' gate/up matrices (all
+    rows) and of rows `down_rows` of their down matrices, from the raw fp32
+    draws (the same draws the GPU tables were encoded from)."""
+    import stq_workloads as W
+    from _oracle_pool import encode_all
+    experts = [int(e) for e in experts]
+    gu_raw = [W.expert_weight_rows(W.TABLE_SEED, e, np.arange(W.N_ROWS)) for e in experts]
+    gu = dict(zip(experts, encode_all(gu_raw, qn)))
+    del gu_raw
+    dn = {e: O.quantize_rows(W.expert_weight_rows(W.DOWN_SEED, e, down_rows, n=W.K, k=W.D_FF)) for e in experts}
+    return gu, dn
+
+
+def test_full_size_token_matches_oracle(stq, full_tables):
+    """d_model 7168, d_ff 2048, 256-expert tables encoded on the GPU; one bf16
+    token routed to 3 experts: the oracle encodes those experts' raw fp32
+    draws itself and computes all 7168 outputs."""
+    import stq_workloads as W
+    tabs_g, tabs_d, qn = full_tables
     experts = [3, 77, 250]
     pe = np.array(experts, dtype=np.int32)
     pw = S.routing_weights(31, 1, 3)
     xb, xf = S.bf16_normal(np.random.default_rng(32), (1, W.K))
-    y = _run(stq, ((tg, sg), (td, sd)), W.N_EXPERTS, W.K, W.D_FF, xb, pe, pw, 3)
-    qn = q.cpu().numpy()
-    gu = {e: O.quantize_rows(W.expert_weight_rows(W.TABLE_SEED, e, np.arange(W.N_ROWS)), qn) for e in experts}
-    dn = {e: O.quantize_rows(W.expert_weight_rows(W.DOWN_SEED, e, np.arange(W.K), n=W.K, k=W.D_FF)) for e in experts}
+    y = _run(stq, (tabs_g, tabs_d), W.N_EXPERTS, W.K, W.D_FF, xb, pe, pw, 3)
+    gu, dn = _oracle_layer(experts, qn, np.arange(W.K))
     _check(y, gu, dn, W.K, W.D_FF, xf, pe, pw, 3)
 
 
-def test_bench_shape_is_linear_in_routing_weights(stq):
+@pytest.mark.parametrize("n_tokens,seed", [(16, 51), (64, 52)])
+def test_full_size_batch_matches_oracle(stq, full_tables, n_tokens, seed):
+    """A decode batch of 16 or 64 tokens, top-8 of 256 experts, at the
+    benchmark's shapes: four sampled tokens' outputs (all eight routed pairs
+    each, 96 sampled output rows) against the oracle, which encodes those
+    tokens' experts from the raw fp32 draws."""
+    import stq_workloads as W
+    (tg, sg), (td, sd), qn = full_tables
+    pe_t, _, pe, _ = W.decode_pairs(seed, n_tokens)
+    pw = S.routing_weights(seed + 1, n_tokens, 8)
+    x = S.torch_bf16_normal(seed + 2, (n_tokens, W.K))
+    y = stq.moe_ffn_decode(tg, sg, td, sd, W.N_EXPERTS, W.K, W.D_FF, x, pe_t,
+                           torch.from_numpy(pw).cuda(), 8).cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(seed)
+    toks = np.unique(np.concatenate([[0, n_tokens - 1], rng.choice(n_tokens, 2, replace=False)]))
+    rows = np.unique(np.concatenate([[0, W.K - 1], rng.integers(0, W.K, 94)]))
+    sel = (toks[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    gu, dn = _oracle_layer(np.unique(pe[sel]), qn, rows)
+    xf = x.float().cpu().numpy()[toks]
+    ref = O.moe_ffn_decode(gu, dn, W.K, W.D_FF, xf, pe[sel], pw[sel], 8, n_out=len(rows))
+    bound = O.moe_ffn_tolerance(gu, dn, W.K, W.D_FF, xf, pe[sel], pw[sel], 8, n_out=len(rows))
+    err = np.abs(y[toks][:, rows] - ref)
+    assert np.all(np.isfinite(ref)) and np.all(err <= bound), float(np.max(err / bound))
+
+
+def test_bench_shape_is_linear_in_routing_weights(stq, full_tables):
     """Batch 16, top-8 of 256 experts at full size: y(w) equals the sum over k
     of w_k times y(one-hot k), up to fp32 rounding of the 8-term combine."""
     import stq_workloads as W
-    tg, sg = W.encode_table(imatrix=W.table_imatrix())
-    td, sd = W.encode_down_table()
+    (tg, sg), (td, sd), _ = full_tables
     pe_t, _, pe, _ = W.decode_pairs(41, 16)
     pw = S.routing_weights(42, 16, 8)
     x = S.torch_bf16_normal(43, (16, W.K))

@@ -517,6 +517,45 @@ def test_tolerance_scale_closed_form():
     assert np.allclose(A, 256.0 * d.sum(axis=1), rtol=0, atol=0)
 
 
+def test_tolerance_scale_signed_inputs_and_scales():
+    """A = sum_b |d_b| sum_{k in b} |x_k| for signed x and scales of either sign.
+    Pins: (1) A bounds |W_hat x| (triangle inequality) and does not depend on
+    the signs of x; (2) for x = sign(w_hat_r) * m (m >= 0, so x vanishes on
+    row r's zero lanes) every term of row r's dot product is |w_hat| m, and
+    the exactly summed y_r equals A_r; (3) putting mass on a zero lane of row r
+    raises A_r by |d| times that mass but leaves y_r unchanged."""
+    n, k = 4, 512
+    nb = k // 256
+    blocks = O.unpack_matrix(_small_packed(10, n, k), n, nb).copy()
+    d16, codes = O.unpack_blocks(blocks.reshape(-1, 42))
+    d16 = d16.reshape(n, nb).copy()
+    d16[1, 0] |= 0x8000                                    # negative scales
+    d16[3, 1] |= 0x8000
+    blocks = O.pack_blocks(d16.reshape(-1), codes).reshape(n, nb, 42)
+    q = O.pack_matrix(blocks)
+    w_hat = O.dequantize_rows(q, n, k).astype(np.float64)
+    assert np.any(w_hat[1, :256] < 0) and np.any(w_hat[3, 256:] > 0)
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 1, k).astype(np.float32)
+    A = O.tolerance_scale(q, n, k, x)[0]
+    assert np.all(A >= np.abs(O.gemv(q, n, k, x)))
+    flips = np.where(rng.random(k) < 0.5, -1.0, 1.0).astype(np.float32)
+    np.testing.assert_array_equal(O.tolerance_scale(q, n, k, x * flips)[0], A)
+    np.testing.assert_array_equal(O.tolerance_scale(q, n, k, -x)[0], A)
+    m = np.abs(x).astype(np.float64)
+    for r in range(n):
+        xr = (np.sign(w_hat[r]) * m).astype(np.float32)   # exact: a sign times an fp32
+        exact = math.fsum(float(w_hat[r, i]) * float(xr[i]) for i in range(k))
+        assert O.tolerance_scale(q, n, k, xr)[0][r] == pytest.approx(exact, rel=1e-14)
+        z = int(np.flatnonzero(w_hat[r] == 0)[0])          # a zero lane of row r
+        xz = xr.copy()
+        xz[z] = np.float32(-3.0)
+        b = z // 256
+        dz = abs(float(O.fp16_bits_to_f32(np.array([d16[r, b]], dtype=np.uint16))[0]))
+        assert O.tolerance_scale(q, n, k, xz)[0][r] == pytest.approx(exact + 3.0 * dz, rel=1e-14)
+        assert O.gemv(q, n, k, xz)[r] == pytest.approx(exact, rel=1e-14)
+
+
 def test_grouped_gemm_matches_per_expert_gemv():
     n, k, E = 16, 512, 4
     rb = O.row_bytes(k)
