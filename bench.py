@@ -379,13 +379,14 @@ def main() -> int:
         ef = torch.empty(N, dtype=torch.float64, device=dev)
         ed = torch.empty(N, dtype=torch.float64, device=dev)
         q2o = torch.empty_like(w0)
-        stq.layer_errors(w0, w0_hat, xc, ef, ed)  # warm (sizes the scratch arena)
+        lws = torch.empty(stq.layer_errors_workspace(N, K, SENS_CALIB), dtype=torch.uint8, device=dev)
+        stq.layer_errors(w0, w0_hat, xc, ef, ed, workspace=lws)  # warm
         stq.q2_roundtrip(w0, q2o)
         reps = 20
         a, b = ev(), ev()
         a.record(stream)
         for _ in range(reps):
-            stq.layer_errors(w0, w0_hat, xc, ef, ed)
+            stq.layer_errors(w0, w0_hat, xc, ef, ed, workspace=lws)
         b.record(stream)
         c, d_ = ev(), ev()
         c.record(stream)

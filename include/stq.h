@@ -39,13 +39,19 @@
  *     no entry point synchronises the host;
  *   - arguments are validated on the host before any launch; a failed check
  *     returns a status and stq_last_error() holds a message (thread-local);
- *   - STQ_E_HIP means a HIP call failed (launch, allocation); device faults
- *     surface at the caller's next synchronisation;
- *   - stq_gemv, stq_moe_ffn_decode and stq_layer_errors share a per-device
- *     scratch arena that grows on demand with hipMalloc and is kept until the
- *     process ends;
- *     calls that may overlap on one device must be issued on one stream from
- *     one host thread at a time.
+ *   - STQ_E_HIP means a HIP call (a launch) failed; device faults surface at
+ *     the caller's next synchronisation;
+ *   - the library allocates no device memory and keeps no device state: the
+ *     entry points that need scratch memory (stq_gemv, stq_moe_ffn_decode,
+ *     stq_layer_errors) take a caller-owned `workspace` of `workspace_bytes`
+ *     bytes, 256-byte aligned, whose required size a host-only query gives
+ *     for the same shapes (stq_gemv_plan, stq_moe_ffn_workspace,
+ *     stq_layer_errors_workspace); a NULL or smaller workspace is refused
+ *     with STQ_E_ARG before any launch.  The workspace is in use until the
+ *     call's work on `stream` completes, so calls that run concurrently need
+ *     workspaces of their own; its contents between calls are meaningless;
+ *   - apart from the thread-local error text the entry points are stateless
+ *     and may be called from any number of host threads.
  */
 #ifndef STQ_H
 #define STQ_H
@@ -100,7 +106,10 @@ int64_t stq_row_bytes(int64_t k);
 stq_status stq_quantize_rows(const float* w, const float* imatrix, int64_t n_rows, int64_t k,
                              int encoder, int rounds, uint8_t* out, stq_stream_t stream);
 
-/* Decode a packed matrix to fp32: out[r, i] = +/-fp32(d) or +0.0 (bit-exact).
+/* Decode a packed matrix to fp32: out[r, i] = +/-fp32(d) or +0.0 (bit-exact),
+ * the weights the format stands for (every weight of a group is -d, 0 or +d
+ * with one zero per group of four, d the block's fp16 scale: lemmy post
+ * 66506, paragraph "Four weights, five bits").
  *   q    packed matrix of n_rows rows (layout above), 2-byte aligned
  *   out  [n_rows, k] fp32, row-major */
 stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, float* out,
@@ -108,7 +117,9 @@ stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, floa
 
 /* Gathered decode GEMV over (token, expert) pairs, the STQ1_0 matmul of the
  * decode path (lemmy post 66506, paragraph "Runtime": STQ1_0 kernels run the
- * expert projections).
+ * expert projections; each token reaches the top 8 of 256 routed experts,
+ * traictory.com "Tencent's 200GB Hy4-preview ...", section "The claim,
+ * stated precisely").
  *   w_table   expert e's packed n x k matrix starts at w_table + e*expert_stride_bytes;
  *             w_table 16-byte aligned, expert_stride_bytes a multiple of 16 and
  *             >= n*row_bytes(k)
@@ -123,22 +134,25 @@ stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, floa
  *             is outside [0, n_experts) or whose token is outside
  *             [0, n_tokens) gets a row of NaN.
  *   y         [n_pairs, n] fp32
+ *   workspace, workspace_bytes  caller-owned scratch for split outputs, at
+ *             least the scratch_bytes stq_gemv_plan reports for these shapes
+ *             on this stream's device (may be NULL when that is 0)
  * Accumulation is fp32 with products exact; the summation order is fixed,
- * so repeated calls give identical bits.  Splitting k across workgroups uses
- * the per-device scratch arena (see the conventions above).  The k split,
- * and the parting of an expert with several tokens into up to one k range
- * per token, are chosen per call from the shapes and the device's CU count;
+ * so repeated calls give identical bits.  The k split, and the parting of an
+ * expert with several tokens into up to one k range per token, are chosen
+ * per call from the shapes and the CU count of the device `stream` runs on;
  * the environment variable STQ_GEMV_PLAN="s,p" (1 <= s <= k/256 splits,
  * 1 <= p <= 8 parts) replaces that choice, for tuning and tests.  Results
  * meet the same tolerance under every plan; their bits depend on the plan. */
 stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts,
                     int64_t n, int64_t k, const void* x, int x_dtype, int64_t x_row_stride,
                     int64_t n_tokens, const int32_t* pair_expert, const int32_t* pair_token,
-                    int64_t n_pairs, float* y, stq_stream_t stream);
+                    int64_t n_pairs, float* y, void* workspace, int64_t workspace_bytes,
+                    stq_stream_t stream);
 
 /* The plan stq_gemv takes for these shapes (host only: no GPU work, and no
- * GPU needed when n_cus > 0), so a caller can size the scratch arena before
- * a capture or check a tuning override.  The three outputs are HOST
+ * GPU needed when n_cus > 0), so a caller can size its workspace or check a
+ * tuning override.  The three outputs are HOST
  * pointers; all must be non-NULL (STQ_E_ARG otherwise).
  *   n_experts, n, k, n_pairs  as for stq_gemv (same checks, same errors)
  *   n_cus        compute units to plan for; 0 = the current device's (256
@@ -146,7 +160,7 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
  *   splits       out: ranges the k blocks of a row are split into
  *   max_parts    out: most k parts one split is cut into for an expert with
  *                several tokens (an expert with m pairs takes min(m, max_parts))
- *   scratch_bytes  out: scratch the call needs (0 when nothing is split)
+ *   scratch_bytes  out: workspace bytes the call needs (0 when nothing is split)
  * STQ_GEMV_PLAN is honoured as in stq_gemv.  n_pairs == 0 or n == 0 gives
  * (1, 1, 0): stq_gemv launches nothing then. */
 stq_status stq_gemv_plan(int64_t n_experts, int64_t n, int64_t k, int64_t n_pairs, int32_t n_cus,
@@ -170,17 +184,32 @@ stq_status stq_gemv_plan(int64_t n_experts, int64_t n, int64_t k, int64_t n_pair
  *   x          bf16 bits [n_tokens, d_model], row-major
  *   pair_expert int32, pair_weight fp32 [n_tokens*top_k], token-major
  *   y          fp32 [n_tokens, d_model]
+ *   workspace, workspace_bytes  caller-owned scratch, at least what
+ *              stq_moe_ffn_workspace reports for these shapes on this
+ *              stream's device: the pairs' gate/up rows, activations and down
+ *              rows (fp32) plus the GEMVs' split outputs
  * Both projections run through the GEMV above (pairs sharing an expert are
- * batched), with h formed once per element between them; intermediates
- * live in the scratch arena.  A pair whose expert is outside
- * [0, n_experts) makes its token's row NaN.  At most 65535 pairs per call. */
+ * batched), with h formed once per element between them.  A pair whose
+ * expert is outside [0, n_experts) makes its token's row NaN.  At most 65535
+ * pairs per call. */
 stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_bytes, const uint8_t* w_down,
                               int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
                               const uint16_t* x, int64_t n_tokens, const int32_t* pair_expert,
-                              const float* pair_weight, int64_t top_k, float* y, stq_stream_t stream);
+                              const float* pair_weight, int64_t top_k, float* y, void* workspace,
+                              int64_t workspace_bytes, stq_stream_t stream);
+
+/* Workspace bytes stq_moe_ffn_decode needs for these shapes on a device with
+ * n_cus compute units (0: the current device's); host only, same checks and
+ * errors as the call.  workspace_bytes is a HOST pointer; 0 when n_tokens is 0. */
+stq_status stq_moe_ffn_workspace(int64_t n_experts, int64_t d_model, int64_t d_ff, int64_t n_tokens,
+                                 int64_t top_k, int32_t n_cus, int64_t* workspace_bytes);
 
 /* Grouped GEMM of the prefill path: tokens routed to each expert,
- * grouped by expert, times that expert's STQ1_0 matrix.
+ * grouped by expert, times that expert's STQ1_0 matrix (lemmy post 66506,
+ * paragraph "Runtime": STQ1_0 kernels run the routed experts' projections;
+ * each token reaches the top 8 of 256 routed experts, traictory.com
+ * "Tencent's 200GB Hy4-preview ...", section "The claim, stated precisely",
+ * so a prompt's tokens form one dense product per expert).
  *   x_sorted        [total_m, k] bf16 bits, row-major, 16-byte aligned rows
  *                   (k*2 bytes apart)
  *   expert_offsets  DEVICE int32 [n_experts+1], non-decreasing, offsets[0] = 0,
@@ -216,11 +245,17 @@ stq_status stq_grouped_gemm(const uint8_t* w_table, int64_t expert_stride_bytes,
  * the matrix cores, so the results agree with an fp64 reference to within
  * the fp64 rounding of sums of k and n_calib terms.  The summation order is
  * fixed: repeated calls give identical bits.  Non-finite inputs give
- * non-finite outputs.  Scratch: 8*(k + 2*ceil(n_calib/64)*n_rows) bytes of
- * the arena. */
+ * non-finite outputs.
+ *   workspace, workspace_bytes  caller-owned scratch of at least
+ *              stq_layer_errors_workspace bytes: 8*(k + 2*ceil(n_calib/64)*n_rows)
+ *              (the diagonal of H, then per-tile partial sums) */
 stq_status stq_layer_errors(const float* w, const float* w_hat, int64_t n_rows, int64_t k,
                             const float* x_calib, int64_t n_calib, double* err_full, double* err_diag,
-                            stq_stream_t stream);
+                            void* workspace, int64_t workspace_bytes, stq_stream_t stream);
+
+/* Workspace bytes stq_layer_errors needs (host only; same checks and errors
+ * as the call; 0 when n_rows is 0).  workspace_bytes is a HOST pointer. */
+stq_status stq_layer_errors_workspace(int64_t n_rows, int64_t k, int64_t n_calib, int64_t* workspace_bytes);
 
 /* Quantize-and-reconstruct through the plain 2-bit format this library uses
  * as the larger partner format of a per-layer allocation (the pages pair

@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "QK", "BLOCK_BYTES", "ENC_WLS", "ENC_AMAX", "StqError", "lib", "lib_path",
     "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "gemv_plan", "grouped_gemm", "moe_ffn_decode",
-    "layer_errors", "q2_roundtrip", "greedy_allocation", "stream_read_probe",
+    "moe_ffn_workspace", "layer_errors", "layer_errors_workspace", "q2_roundtrip", "greedy_allocation",
+    "stream_read_probe",
 ]
 
 QK = 256
@@ -64,7 +65,7 @@ def lib() -> ctypes.CDLL:
     L.stq_dequantize_rows.argtypes = [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]
     L.stq_dequantize_rows.restype = _c_int
     L.stq_gemv.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_i64, _c_i64,
-                           _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
+                           _c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]
     L.stq_gemv.restype = _c_int
     L.stq_gemv_plan.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(_c_i64)]
@@ -72,10 +73,16 @@ def lib() -> ctypes.CDLL:
     L.stq_grouped_gemm.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
     L.stq_grouped_gemm.restype = _c_int
     L.stq_moe_ffn_decode.argtypes = [_c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
-                                     _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
+                                     _c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]
     L.stq_moe_ffn_decode.restype = _c_int
-    L.stq_layer_errors.argtypes = [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp]
+    L.stq_moe_ffn_workspace.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int32,
+                                        ctypes.POINTER(_c_i64)]
+    L.stq_moe_ffn_workspace.restype = _c_int
+    L.stq_layer_errors.argtypes = [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_i64,
+                                   _c_vp]
     L.stq_layer_errors.restype = _c_int
+    L.stq_layer_errors_workspace.argtypes = [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_i64)]
+    L.stq_layer_errors_workspace.restype = _c_int
     L.stq_q2_roundtrip.argtypes = [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]
     L.stq_q2_roundtrip.restype = _c_int
     L.stq_greedy_allocation.argtypes = [_c_vp, _c_vp, _c_i64, ctypes.c_double, _c_vp]
@@ -93,6 +100,17 @@ def _check(func: str, status: int) -> None:
 
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
+
+
+_CUS: dict = {}
+
+
+def _device_cus(device) -> int:
+    """Compute units of a GPU tensor's device, the count the library plans the GEMV for."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _CUS:
+        _CUS[idx] = torch.cuda.get_device_properties(idx).multi_processor_count
+    return _CUS[idx]
 
 
 def _ptr(t) -> int | None:
@@ -113,6 +131,20 @@ def _holds(name: str, t: torch.Tensor, n: int) -> None:
     written past its end, so it is refused here."""
     if t.numel() < n:
         raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
+def _workspace(ws: torch.Tensor | None, need: int, device) -> torch.Tensor | None:
+    """A caller's workspace (checked) or a new one from torch's caching allocator; its memory
+    is ordered on the current stream, like every other tensor the call takes."""
+    if ws is None:
+        return torch.empty(need, dtype=torch.uint8, device=device) if need > 0 else None
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ws
+
+
+def _ws_args(ws: torch.Tensor | None) -> tuple:
+    return (None, 0) if ws is None else (ws.data_ptr(), ws.numel() * ws.element_size())
 
 
 def _table(name: str, t: torch.Tensor, n_experts: int, stride: int, n: int, k: int) -> None:
@@ -170,8 +202,10 @@ def gemv_plan(n_experts: int, n: int, k: int, n_pairs: int, n_cus: int = 0) -> t
 
 def gemv(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: int, k: int, x: torch.Tensor,
          pair_expert: torch.Tensor | None = None, pair_token: torch.Tensor | None = None,
-         n_pairs: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
-    """y[i] = W_{pair_expert[i]} x[pair_token[i]] for every pair; x is [n_tokens, k] fp32 or bf16."""
+         n_pairs: int | None = None, out: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y[i] = W_{pair_expert[i]} x[pair_token[i]] for every pair; x is [n_tokens, k] fp32 or bf16.
+    `workspace` (GPU bytes, at least gemv_plan(...)[2]) is allocated here when not given."""
     _on_gpu("w_table", w_table, torch.uint8)
     if x.dtype == torch.bfloat16:
         xd = X_BF16
@@ -201,9 +235,15 @@ def gemv(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: int, k: i
         _table("w_table", w_table, n_experts, expert_stride, n, k)
     # a one-row view may carry any stride in its first dimension; its rows are k apart
     x_stride = x.stride(0) if n_tokens > 1 else x.shape[1]
+    if workspace is None and int(n_pairs) > 0 and int(n) > 0:
+        need = gemv_plan(n_experts, n, k, n_pairs, _device_cus(x.device))[2]
+        workspace = _workspace(None, need, x.device)
+    else:
+        workspace = _workspace(workspace, 0, x.device)
     _check("stq_gemv", lib().stq_gemv(w_table.data_ptr(), int(expert_stride), int(n_experts), int(n), int(k),
                                       x.data_ptr(), xd, x_stride, n_tokens, _ptr(pair_expert),
-                                      _ptr(pair_token), int(n_pairs), out.data_ptr(), _stream()))
+                                      _ptr(pair_token), int(n_pairs), out.data_ptr(), *_ws_args(workspace),
+                                      _stream()))
     return out
 
 
@@ -230,11 +270,23 @@ def grouped_gemm(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: i
     return out
 
 
+def moe_ffn_workspace(n_experts: int, d_model: int, d_ff: int, n_tokens: int, top_k: int, n_cus: int = 0) -> int:
+    """Workspace bytes moe_ffn_decode needs for these shapes on n_cus compute units (0: the
+    current device's); host only."""
+    wb = ctypes.c_int64()
+    _check("stq_moe_ffn_workspace", lib().stq_moe_ffn_workspace(int(n_experts), int(d_model), int(d_ff),
+                                                                int(n_tokens), int(top_k), int(n_cus),
+                                                                ctypes.byref(wb)))
+    return wb.value
+
+
 def moe_ffn_decode(w_gate_up: torch.Tensor, gate_up_stride: int, w_down: torch.Tensor, down_stride: int,
                    n_experts: int, d_model: int, d_ff: int, x: torch.Tensor, pair_expert: torch.Tensor,
-                   pair_weight: torch.Tensor, top_k: int, out: torch.Tensor | None = None) -> torch.Tensor:
+                   pair_weight: torch.Tensor, top_k: int, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Routed-expert FFN for decode tokens x bf16 [T, d_model]: per token, the routing-weighted sum
-    over its top_k pairs of W_down_e (silu(W_gate_e x) * (W_up_e x)); pairs token-major [T*top_k]."""
+    over its top_k pairs of W_down_e (silu(W_gate_e x) * (W_up_e x)); pairs token-major [T*top_k].
+    `workspace` (GPU bytes, at least moe_ffn_workspace(...)) is allocated here when not given."""
     _on_gpu("w_gate_up", w_gate_up, torch.uint8)
     _on_gpu("w_down", w_down, torch.uint8)
     _on_gpu("x", x, torch.bfloat16)
@@ -252,18 +304,33 @@ def moe_ffn_decode(w_gate_up: torch.Tensor, gate_up_stride: int, w_down: torch.T
     if n_tokens > 0:
         _table("w_gate_up", w_gate_up, n_experts, gate_up_stride, 2 * int(d_ff), d_model)
         _table("w_down", w_down, n_experts, down_stride, d_model, d_ff)
+    if workspace is None and n_tokens > 0:
+        need = moe_ffn_workspace(n_experts, d_model, d_ff, n_tokens, top_k, _device_cus(x.device))
+        workspace = _workspace(None, need, x.device)
+    else:
+        workspace = _workspace(workspace, 0, x.device)
     _check("stq_moe_ffn_decode",
            lib().stq_moe_ffn_decode(w_gate_up.data_ptr(), int(gate_up_stride), w_down.data_ptr(), int(down_stride),
                                     int(n_experts), int(d_model), int(d_ff), x.data_ptr(), n_tokens,
                                     pair_expert.data_ptr(), pair_weight.data_ptr(), int(top_k), out.data_ptr(),
-                                    _stream()))
+                                    *_ws_args(workspace), _stream()))
     return out
 
 
+def layer_errors_workspace(n_rows: int, k: int, n_calib: int) -> int:
+    """Workspace bytes layer_errors needs for these shapes (host only)."""
+    wb = ctypes.c_int64()
+    _check("stq_layer_errors_workspace", lib().stq_layer_errors_workspace(int(n_rows), int(k), int(n_calib),
+                                                                          ctypes.byref(wb)))
+    return wb.value
+
+
 def layer_errors(w: torch.Tensor, w_hat: torch.Tensor, x_calib: torch.Tensor,
-                 out_full: torch.Tensor | None = None, out_diag: torch.Tensor | None = None):
+                 out_full: torch.Tensor | None = None, out_diag: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None):
     """Per-row error of w_hat against w under calibration rows x_calib fp32 [N, k]: full-Hessian
-    sum_i ((w - w_hat) . x_i)^2 and diagonal sum_c H_cc (w - w_hat)_c^2, both fp64 [n]."""
+    sum_i ((w - w_hat) . x_i)^2 and diagonal sum_c H_cc (w - w_hat)_c^2, both fp64 [n].
+    `workspace` (GPU bytes, at least layer_errors_workspace(...)) is allocated here when not given."""
     _on_gpu("w", w, torch.float32)
     _on_gpu("w_hat", w_hat, torch.float32)
     _on_gpu("x_calib", x_calib, torch.float32)
@@ -278,9 +345,13 @@ def layer_errors(w: torch.Tensor, w_hat: torch.Tensor, x_calib: torch.Tensor,
     _on_gpu("out_diag", out_diag, torch.float64)
     if out_full.numel() < n or out_diag.numel() < n:
         raise ValueError("outputs must hold n entries")
+    if workspace is None and n > 0 and x_calib.shape[0] > 0:
+        workspace = _workspace(None, layer_errors_workspace(n, k, x_calib.shape[0]), w.device)
+    else:
+        workspace = _workspace(workspace, 0, w.device)
     _check("stq_layer_errors", lib().stq_layer_errors(w.data_ptr(), w_hat.data_ptr(), n, k, x_calib.data_ptr(),
                                                       x_calib.shape[0], out_full.data_ptr(), out_diag.data_ptr(),
-                                                      _stream()))
+                                                      *_ws_args(workspace), _stream()))
     return out_full, out_diag
 
 

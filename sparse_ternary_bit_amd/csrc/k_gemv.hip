@@ -622,11 +622,10 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 
 }  // namespace
 
-// Compute units of the current device (cached per device; 256 if the query fails).
-static int device_cus() {
+// Compute units of device `dev` (cached per device; 256 if the query fails).
+static int cus_of_device(int dev) {
   static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 0) return 256;
   if (dev < 64) {
     const int c = cache[dev].load(std::memory_order_relaxed);
     if (c > 0) return c;
@@ -635,6 +634,18 @@ static int device_cus() {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+int cus_of_stream(hipStream_t s) {
+  int dev = -1;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess) return 256;
+  return cus_of_device(dev);
+}
+
+int cus_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  return cus_of_device(dev);
 }
 
 // Work of one pass over a block, relative to a one-token pass, for a pass
@@ -722,14 +733,14 @@ static void estimate_plan(const GemvArgs& a, int cus, int& best_splits, int& bes
 
 // The estimate depends only on the shapes and the CU count; decode loops
 // repeat a few shapes, so each host thread keeps its last 16 answers.
-GemvPlan plan_gemv(const GemvArgs& a, int for_cus) {
+GemvPlan plan_gemv(const GemvArgs& a, int cus) {
   struct Entry {
     int64_t n_pairs, n_experts, n, k;
     int cus, splits, bps, sub;
   };
   thread_local Entry cache[16];
   thread_local int cache_used = 0, cache_next = 0;
-  const int cus = for_cus > 0 ? for_cus : device_cus();
+  if (cus <= 0) cus = 256;
   const int nb = static_cast<int>(a.k / kQK);
   const bool parts_ok = a.n_experts <= kLeadExperts;
   int best_splits = 0, best_bps = 0, best_sub = 0;

@@ -7,9 +7,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
-#include <mutex>
 #include <string>
-#include <unordered_map>
 #include <vector>
 
 #include "stq.h"
@@ -40,39 +38,16 @@ stq_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Per-device scratch arena for split-k partial sums and the FFN's
-// intermediates: grown with hipMalloc when a call needs more (hipFree of the
-// old arena waits for work that may still use it) and kept until the
-// process ends.
-struct Arena {
-  void* ptr = nullptr;
-  int64_t cap = 0;
-};
-std::mutex g_arena_mu;
-std::unordered_map<int, Arena> g_arena;
-
-stq_status arena_get(int64_t bytes, void** out, const char* who) {
-  *out = nullptr;
-  if (bytes <= 0) return STQ_OK;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, who);
-  std::lock_guard<std::mutex> lk(g_arena_mu);
-  Arena& a = g_arena[dev];
-  if (a.cap < bytes) {
-    if (a.ptr) {
-      e = hipFree(a.ptr);
-      a.ptr = nullptr;
-      a.cap = 0;
-      if (e != hipSuccess) return hip_fail(e, who);
-    }
-    void* p = nullptr;
-    e = hipMalloc(&p, static_cast<size_t>(bytes));
-    if (e != hipSuccess) return hip_fail(e, who);
-    a.ptr = p;
-    a.cap = bytes;
-  }
-  *out = a.ptr;
+// Caller-owned workspace: a call that needs `need` bytes accepts any buffer
+// of at least that many bytes, 256-byte aligned (the kernels read partial
+// sums 16 bytes at a time and sub-buffers start on 256-byte boundaries).
+stq_status check_workspace(const void* ws, int64_t ws_bytes, int64_t need, const char* who) {
+  if (ws_bytes < 0) return fail(STQ_E_ARG, "%s: workspace_bytes < 0", who);
+  if (need <= 0) return STQ_OK;
+  if (!ws || ws_bytes < need)
+    return fail(STQ_E_ARG, "%s: needs a workspace of %lld bytes, got %lld%s", who, (long long)need,
+                (long long)ws_bytes, ws ? "" : " (NULL)");
+  if (!aligned(ws, 256)) return fail(STQ_E_ALIGN, "%s: workspace not 256-byte aligned", who);
   return STQ_OK;
 }
 
@@ -131,7 +106,7 @@ stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, floa
 stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts, int64_t n, int64_t k,
                     const void* x, int x_dtype, int64_t x_row_stride, int64_t n_tokens,
                     const int32_t* pair_expert, const int32_t* pair_token, int64_t n_pairs, float* y,
-                    stq_stream_t stream) {
+                    void* workspace, int64_t workspace_bytes, stq_stream_t stream) {
   if (n_experts < 1 || n < 0 || n_tokens < 0 || n_pairs < 0) return fail(STQ_E_ARG, "stq_gemv: negative count or no experts");
   if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "stq_gemv: k=%lld is not a positive multiple of 256", (long long)k);
   if (x_dtype != STQ_X_F32 && x_dtype != STQ_X_BF16) return fail(STQ_E_ARG, "stq_gemv: unknown x_dtype %d", x_dtype);
@@ -140,19 +115,20 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
   const int64_t rb = stq_row_bytes(k);
   if (expert_stride_bytes < n * rb) return fail(STQ_E_SHAPE, "stq_gemv: expert stride %lld < n*row_bytes %lld", (long long)expert_stride_bytes, (long long)(n * rb));
   if (x_row_stride < k) return fail(STQ_E_SHAPE, "stq_gemv: x_row_stride < k");
+  if (workspace_bytes < 0) return fail(STQ_E_ARG, "stq_gemv: workspace_bytes < 0");
   if (n_pairs == 0 || n == 0) return ok();
   if (!w_table || !x || !y) return fail(STQ_E_ARG, "stq_gemv: null pointer");
   if (!aligned(w_table, 16) || expert_stride_bytes % 16) return fail(STQ_E_ALIGN, "stq_gemv: w_table / expert stride not 16-byte aligned");
   if (!aligned(x, 4) || !aligned(y, 4) || !aligned(pair_expert, 4) || !aligned(pair_token, 4)) return fail(STQ_E_ALIGN, "stq_gemv: x, y or pair arrays not 4-byte aligned");
   if (x_dtype == STQ_X_BF16 && (x_row_stride % 2)) return fail(STQ_E_ALIGN, "stq_gemv: bf16 x_row_stride must be even");
 
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   stq::GemvArgs ga{w_table, expert_stride_bytes, n_experts, n, k, x, x_dtype == STQ_X_BF16 ? 1 : 0,
                    x_row_stride, n_tokens, pair_expert, pair_token, n_pairs, y, 1};
-  const stq::GemvPlan pl = stq::plan_gemv(ga);
-  void* partial = nullptr;
-  const stq_status st = arena_get(pl.partial_bytes, &partial, "stq_gemv: scratch");
+  const stq::GemvPlan pl = stq::plan_gemv(ga, stq::cus_of_stream(s));
+  const stq_status st = check_workspace(workspace, workspace_bytes, pl.partial_bytes, "stq_gemv");
   if (st != STQ_OK) return st;
-  hipError_t le = stq::launch_gemv(ga, pl, partial, reinterpret_cast<hipStream_t>(stream));
+  hipError_t le = stq::launch_gemv(ga, pl, workspace, s);
   if (le != hipSuccess) return hip_fail(le, "stq_gemv launch");
   return ok();
 }
@@ -170,24 +146,80 @@ stq_status stq_gemv_plan(int64_t n_experts, int64_t n, int64_t k, int64_t n_pair
   if (n_pairs == 0 || n == 0) return ok();  // stq_gemv launches nothing
   const stq::GemvArgs ga{nullptr, n * stq_row_bytes(k), n_experts, n, k, nullptr, 1, k, 1, nullptr, nullptr,
                          n_pairs, nullptr, 1};
-  const stq::GemvPlan pl = stq::plan_gemv(ga, n_cus);
+  const stq::GemvPlan pl = stq::plan_gemv(ga, n_cus > 0 ? n_cus : stq::cus_of_current_device());
   *splits = pl.splits;
   *max_parts = pl.max_sub;
   *scratch_bytes = pl.partial_bytes;
   return ok();
 }
 
+namespace {
+
+// Shape checks shared by stq_moe_ffn_decode and its workspace query.
+stq_status ffn_shape_check(int64_t n_experts, int64_t d_model, int64_t d_ff, int64_t n_tokens, int64_t top_k,
+                           const char* who) {
+  if (n_experts < 1 || n_tokens < 0 || top_k < 1) return fail(STQ_E_ARG, "%s: bad count (n_experts >= 1, n_tokens >= 0, top_k >= 1)", who);
+  if (d_model <= 0 || d_model % STQ_QK || d_ff <= 0 || d_ff % STQ_QK)
+    return fail(STQ_E_SHAPE, "%s: d_model and d_ff must be positive multiples of 256", who);
+  if (d_model > INT_MAX / 2 || 2 * d_ff > INT_MAX || n_experts > INT_MAX) return fail(STQ_E_SHAPE, "%s: size exceeds int32", who);
+  if (n_tokens > 65535 / top_k) return fail(STQ_E_SHAPE, "%s: more than 65535 (token, expert) pairs", who);
+  return STQ_OK;
+}
+
+// The FFN's workspace: the two GEMVs' split outputs (one region, reused),
+// then the gate/up rows, the activations and the down projections' rows of
+// every pair, each on a 256-byte boundary.
+struct FfnLayout {
+  stq::GemvArgs g1, g2;
+  stq::GemvPlan p1, p2;
+  int64_t part, gu, h, z, total;
+};
+
+FfnLayout ffn_layout(const uint8_t* w_gate_up, int64_t gate_up_stride_bytes, const uint8_t* w_down,
+                     int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff, const uint16_t* x,
+                     int64_t n_tokens, const int32_t* pair_expert, int64_t top_k, int cus) {
+  FfnLayout L{};
+  const int64_t P = n_tokens * top_k;
+  L.g1 = stq::GemvArgs{w_gate_up, gate_up_stride_bytes, n_experts, 2 * d_ff, d_model, x, 1, d_model, n_tokens,
+                       pair_expert, nullptr, P, nullptr, top_k};
+  L.g2 = stq::GemvArgs{w_down, down_stride_bytes, n_experts, d_model, d_ff, nullptr, 0, d_ff, P,
+                       pair_expert, nullptr, P, nullptr, 1};
+  L.p1 = stq::plan_gemv(L.g1, cus);
+  L.p2 = stq::plan_gemv(L.g2, cus);
+  L.part = round256(std::max(L.p1.partial_bytes, L.p2.partial_bytes));
+  L.gu = round256(P * 2 * d_ff * 4);
+  L.h = round256(P * d_ff * 4);
+  L.z = round256(P * d_model * 4);
+  L.total = P == 0 ? 0 : L.part + L.gu + L.h + L.z;
+  return L;
+}
+
+}  // namespace
+
+stq_status stq_moe_ffn_workspace(int64_t n_experts, int64_t d_model, int64_t d_ff, int64_t n_tokens, int64_t top_k,
+                                 int32_t n_cus, int64_t* workspace_bytes) {
+  if (!workspace_bytes) return fail(STQ_E_ARG, "stq_moe_ffn_workspace: null output pointer");
+  *workspace_bytes = 0;
+  if (n_cus < 0) return fail(STQ_E_ARG, "stq_moe_ffn_workspace: n_cus < 0");
+  const stq_status st = ffn_shape_check(n_experts, d_model, d_ff, n_tokens, top_k, "stq_moe_ffn_workspace");
+  if (st != STQ_OK) return st;
+  const FfnLayout L = ffn_layout(nullptr, 2 * d_ff * stq_row_bytes(d_model), nullptr, d_model * stq_row_bytes(d_ff),
+                                 n_experts, d_model, d_ff, nullptr, n_tokens, nullptr, top_k,
+                                 n_cus > 0 ? n_cus : stq::cus_of_current_device());
+  *workspace_bytes = L.total;
+  return ok();
+}
+
 stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_bytes, const uint8_t* w_down,
                               int64_t down_stride_bytes, int64_t n_experts, int64_t d_model, int64_t d_ff,
                               const uint16_t* x, int64_t n_tokens, const int32_t* pair_expert,
-                              const float* pair_weight, int64_t top_k, float* y, stq_stream_t stream) {
-  if (n_experts < 1 || n_tokens < 0 || top_k < 1) return fail(STQ_E_ARG, "stq_moe_ffn_decode: bad count (n_experts >= 1, n_tokens >= 0, top_k >= 1)");
-  if (d_model <= 0 || d_model % STQ_QK || d_ff <= 0 || d_ff % STQ_QK)
-    return fail(STQ_E_SHAPE, "stq_moe_ffn_decode: d_model and d_ff must be positive multiples of 256");
-  if (d_model > INT_MAX / 2 || 2 * d_ff > INT_MAX || n_experts > INT_MAX) return fail(STQ_E_SHAPE, "stq_moe_ffn_decode: size exceeds int32");
-  if (n_tokens > 65535 / top_k) return fail(STQ_E_SHAPE, "stq_moe_ffn_decode: more than 65535 (token, expert) pairs");
+                              const float* pair_weight, int64_t top_k, float* y, void* workspace,
+                              int64_t workspace_bytes, stq_stream_t stream) {
+  const stq_status sc = ffn_shape_check(n_experts, d_model, d_ff, n_tokens, top_k, "stq_moe_ffn_decode");
+  if (sc != STQ_OK) return sc;
   if (gate_up_stride_bytes < 2 * d_ff * stq_row_bytes(d_model) || down_stride_bytes < d_model * stq_row_bytes(d_ff))
     return fail(STQ_E_SHAPE, "stq_moe_ffn_decode: expert stride smaller than the packed matrix");
+  if (workspace_bytes < 0) return fail(STQ_E_ARG, "stq_moe_ffn_decode: workspace_bytes < 0");
   if (n_tokens == 0) return ok();
   if (!w_gate_up || !w_down || !x || !pair_expert || !pair_weight || !y) return fail(STQ_E_ARG, "stq_moe_ffn_decode: null pointer");
   if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || gate_up_stride_bytes % 16 || down_stride_bytes % 16)
@@ -195,39 +227,31 @@ stq_status stq_moe_ffn_decode(const uint8_t* w_gate_up, int64_t gate_up_stride_b
   if (!aligned(x, 4) || !aligned(pair_expert, 4) || !aligned(pair_weight, 4) || !aligned(y, 4))
     return fail(STQ_E_ALIGN, "stq_moe_ffn_decode: x, pair arrays or y not 4-byte aligned");
 
-  const int64_t P = n_tokens * top_k;
-  // gate/up GEMV of every pair's token, SwiGLU of each gate/up row, then the
-  // down GEMV of every pair's activation row
-  stq::GemvArgs g1{w_gate_up, gate_up_stride_bytes, n_experts, 2 * d_ff, d_model, x, 1, d_model, n_tokens,
-                   pair_expert, nullptr, P, nullptr, top_k};
-  stq::GemvArgs g2{w_down, down_stride_bytes, n_experts, d_model, d_ff, nullptr, 0, d_ff, P,
-                   pair_expert, nullptr, P, nullptr, 1};
-  const stq::GemvPlan p1 = stq::plan_gemv(g1), p2 = stq::plan_gemv(g2);
-  const int64_t part = round256(std::max(p1.partial_bytes, p2.partial_bytes));
-  const int64_t gu_bytes = round256(P * 2 * d_ff * 4);
-  const int64_t h_bytes = round256(P * d_ff * 4);
-  const int64_t z_bytes = round256(P * d_model * 4);
-  void* base = nullptr;
-  const stq_status st = arena_get(part + gu_bytes + h_bytes + z_bytes, &base, "stq_moe_ffn_decode: scratch");
-  if (st != STQ_OK) return st;
-  char* b = static_cast<char*>(base);
-  float* gu = reinterpret_cast<float*>(b + part);
-  float* h = reinterpret_cast<float*>(b + part + gu_bytes);
-  float* z = reinterpret_cast<float*>(b + part + gu_bytes + h_bytes);
-  g1.y = gu;
-  g2.x = h;
-  g2.y = z;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // each GEMV's split outputs are added by the next step (SwiGLU, combine)
-  // instead of a reduction launch of its own; the order of the adds is the same
-  hipError_t e = stq::launch_gemv(g1, p1, b, s, false);
+  FfnLayout L = ffn_layout(w_gate_up, gate_up_stride_bytes, w_down, down_stride_bytes, n_experts, d_model, d_ff, x,
+                           n_tokens, pair_expert, top_k, stq::cus_of_stream(s));
+  const stq_status st = check_workspace(workspace, workspace_bytes, L.total, "stq_moe_ffn_decode");
+  if (st != STQ_OK) return st;
+  const int64_t P = n_tokens * top_k;
+  char* b = static_cast<char*>(workspace);
+  float* gu = reinterpret_cast<float*>(b + L.part);
+  float* h = reinterpret_cast<float*>(b + L.part + L.gu);
+  float* z = reinterpret_cast<float*>(b + L.part + L.gu + L.h);
+  L.g1.y = gu;
+  L.g2.x = h;
+  L.g2.y = z;
+  // gate/up GEMV of every pair's token, SwiGLU of each gate/up row, then the
+  // down GEMV of every pair's activation row; each GEMV's split outputs are
+  // added by the next step (SwiGLU, combine) instead of a reduction launch of
+  // its own, in the same order
+  hipError_t e = stq::launch_gemv(L.g1, L.p1, b, s, false);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: gate/up launch");
-  e = stq::launch_swiglu(gu, stq::gemv_partials(p1, b), pair_expert, n_experts, P, d_ff, h, s);
+  e = stq::launch_swiglu(gu, stq::gemv_partials(L.p1, b), pair_expert, n_experts, P, d_ff, h, s);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: SwiGLU launch");
-  e = stq::launch_gemv(g2, p2, b, s, false);
+  e = stq::launch_gemv(L.g2, L.p2, b, s, false);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: down launch");
-  e = stq::launch_combine(z, stq::gemv_partials(p2, b), pair_expert, n_experts, pair_weight, n_tokens, top_k,
-                                d_model, y, s);
+  e = stq::launch_combine(z, stq::gemv_partials(L.p2, b), pair_expert, n_experts, pair_weight, n_tokens, top_k,
+                          d_model, y, s);
   if (e != hipSuccess) return hip_fail(e, "stq_moe_ffn_decode: combine launch");
   return ok();
 }
@@ -253,23 +277,44 @@ stq_status stq_grouped_gemm(const uint8_t* w_table, int64_t expert_stride_bytes,
   return ok();
 }
 
+namespace {
+
+stq_status layer_errors_shape_check(int64_t n_rows, int64_t k, int64_t n_calib, const char* who) {
+  if (n_rows < 0) return fail(STQ_E_ARG, "%s: n_rows < 0", who);
+  if (n_calib < 1) return fail(STQ_E_ARG, "%s: n_calib must be >= 1", who);
+  if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "%s: k=%lld is not a positive multiple of 256", who, (long long)k);
+  if (n_rows > INT_MAX || n_calib > INT_MAX) return fail(STQ_E_SHAPE, "%s: count exceeds int32", who);
+  if ((n_calib + 63) / 64 > 65535) return fail(STQ_E_SHAPE, "%s: more than 65535*64 calibration rows", who);
+  if (((n_rows + 511) / 512) * 8 * ((n_calib + 63) / 64) > INT_MAX) return fail(STQ_E_SHAPE, "%s: too many tiles", who);
+  return STQ_OK;
+}
+
+}  // namespace
+
+stq_status stq_layer_errors_workspace(int64_t n_rows, int64_t k, int64_t n_calib, int64_t* workspace_bytes) {
+  if (!workspace_bytes) return fail(STQ_E_ARG, "stq_layer_errors_workspace: null output pointer");
+  *workspace_bytes = 0;
+  const stq_status st = layer_errors_shape_check(n_rows, k, n_calib, "stq_layer_errors_workspace");
+  if (st != STQ_OK) return st;
+  *workspace_bytes = n_rows == 0 ? 0 : stq::layer_errors_scratch_bytes(n_rows, k, n_calib);
+  return ok();
+}
+
 stq_status stq_layer_errors(const float* w, const float* w_hat, int64_t n_rows, int64_t k, const float* x_calib,
-                            int64_t n_calib, double* err_full, double* err_diag, stq_stream_t stream) {
-  if (n_rows < 0) return fail(STQ_E_ARG, "stq_layer_errors: n_rows < 0");
-  if (n_calib < 1) return fail(STQ_E_ARG, "stq_layer_errors: n_calib must be >= 1");
-  if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "stq_layer_errors: k=%lld is not a positive multiple of 256", (long long)k);
-  if (n_rows > INT_MAX || n_calib > INT_MAX) return fail(STQ_E_SHAPE, "stq_layer_errors: count exceeds int32");
-  if ((n_calib + 63) / 64 > 65535) return fail(STQ_E_SHAPE, "stq_layer_errors: more than 65535*64 calibration rows");
-  if (((n_rows + 511) / 512) * 8 * ((n_calib + 63) / 64) > INT_MAX) return fail(STQ_E_SHAPE, "stq_layer_errors: too many tiles");
+                            int64_t n_calib, double* err_full, double* err_diag, void* workspace,
+                            int64_t workspace_bytes, stq_stream_t stream) {
+  const stq_status sc = layer_errors_shape_check(n_rows, k, n_calib, "stq_layer_errors");
+  if (sc != STQ_OK) return sc;
+  if (workspace_bytes < 0) return fail(STQ_E_ARG, "stq_layer_errors: workspace_bytes < 0");
   if (n_rows == 0) return ok();
   if (!w || !w_hat || !x_calib || !err_full || !err_diag) return fail(STQ_E_ARG, "stq_layer_errors: null pointer");
   if (!aligned(w, 16) || !aligned(w_hat, 16) || !aligned(x_calib, 16))
     return fail(STQ_E_ALIGN, "stq_layer_errors: w, w_hat and x_calib must be 16-byte aligned");
   if (!aligned(err_full, 8) || !aligned(err_diag, 8)) return fail(STQ_E_ALIGN, "stq_layer_errors: outputs not 8-byte aligned");
-  void* scratch = nullptr;
-  const stq_status st = arena_get(stq::layer_errors_scratch_bytes(n_rows, k, n_calib), &scratch, "stq_layer_errors: scratch");
+  const stq_status st = check_workspace(workspace, workspace_bytes, stq::layer_errors_scratch_bytes(n_rows, k, n_calib),
+                                        "stq_layer_errors");
   if (st != STQ_OK) return st;
-  hipError_t e = stq::launch_layer_errors(w, w_hat, n_rows, k, x_calib, n_calib, err_full, err_diag, scratch,
+  hipError_t e = stq::launch_layer_errors(w, w_hat, n_rows, k, x_calib, n_calib, err_full, err_diag, workspace,
                                           reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "stq_layer_errors launch");
   return ok();

@@ -39,8 +39,12 @@ struct GemvPlan {
   int64_t partial_floats;
   int64_t partial_bytes;
 };
-// cus: compute units the plan is made for (0: the current device's).
-GemvPlan plan_gemv(const GemvArgs& a, int cus = 0);
+// cus: compute units the plan is made for (see cus_of_stream).
+GemvPlan plan_gemv(const GemvArgs& a, int cus);
+// Compute units of the device a stream runs on, or of the current device
+// (256 when the query fails); cached per device.
+int cus_of_stream(hipStream_t s);
+int cus_of_current_device();
 // reduce = false leaves split outputs in `partial` for the caller to add (see
 // GemvPartials); the GEMV still writes y's rows that are not split and the
 // NaN rows of invalid pairs.

@@ -80,10 +80,10 @@ def test_dequantize_rejects_bad_arguments(L):
 
 def _gemv(L, **kw):
     a = dict(w=FAKE, stride=4096 * 1176, ne=4, n=4096, k=7168, x=FAKE, xd=1, xs=7168, nt=4,
-             pe=None, pt=None, np_=4, y=FAKE)
+             pe=None, pt=None, np_=4, y=FAKE, ws=None, wsb=0)
     a.update(kw)
     return L.stq_gemv(a["w"], a["stride"], a["ne"], a["n"], a["k"], a["x"], a["xd"], a["xs"], a["nt"],
-                      a["pe"], a["pt"], a["np_"], a["y"], None)
+                      a["pe"], a["pt"], a["np_"], a["y"], a["ws"], a["wsb"], None)
 
 
 def test_gemv_rejects_bad_arguments(L):
@@ -99,6 +99,18 @@ def test_gemv_rejects_bad_arguments(L):
     assert _gemv(L, xs=7169) == 3
     assert _gemv(L, y=None) == 1
     assert _gemv(L, np_=-1) == 1
+
+
+def test_gemv_refuses_missing_or_small_workspace(L, monkeypatch):
+    monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    st, (sp, mp, need) = _plan(L, ne=4, np_=4)
+    assert st == 0 and need > 0                       # four single-token experts: k is split
+    assert _gemv(L) == 1 and "workspace" in _err(L)
+    assert _gemv(L, ws=FAKE, wsb=need - 1) == 1 and str(need) in _err(L)
+    assert _gemv(L, ws=FAKE + 16, wsb=need) == 3
+    assert _gemv(L, ws=FAKE, wsb=-1) == 1
+    monkeypatch.setenv("STQ_GEMV_PLAN", "1,1")       # no split: no workspace needed, none checked
+    assert _plan(L, ne=4, np_=4)[1][2] == 0
 
 
 def test_gemv_empty_work_is_ok_without_gpu(L):
@@ -232,12 +244,8 @@ def test_moe_ffn_rejects_bad_arguments(L):
         a = dict(wg=FAKE, gs=gu_stride, wd=FAKE, ds=dn_stride, ne=256, dm=7168, ff=2048, x=FAKE, t=4,
                  pe=FAKE, pw=FAKE, k=8, y=FAKE)
         a.update(kw)
-        L.stq_moe_ffn_decode.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
-                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
-                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                         ctypes.c_void_p, ctypes.c_void_p]
         return L.stq_moe_ffn_decode(a["wg"], a["gs"], a["wd"], a["ds"], a["ne"], a["dm"], a["ff"], a["x"], a["t"],
-                                    a["pe"], a["pw"], a["k"], a["y"], None)
+                                    a["pe"], a["pw"], a["k"], a["y"], a.get("ws"), a.get("wsb", 0), None)
     assert f(dm=7000) == 2
     assert f(ff=100) == 2
     assert f(k=0) == 1
@@ -250,20 +258,86 @@ def test_moe_ffn_rejects_bad_arguments(L):
     assert f(gs=gu_stride + 8) == 3
     assert f(x=FAKE + 2) == 3
     assert f(t=0, wg=None, wd=None, x=None, pe=None, pw=None, y=None) == 0
+    assert f(wsb=-1) == 1
+
+
+def _ffn_ws(L, ne=256, dm=7168, ff=2048, t=4, k=8, cus=256):
+    wb = ctypes.c_int64(-7)
+    st = L.stq_moe_ffn_workspace(ne, dm, ff, t, k, cus, ctypes.byref(wb))
+    return st, wb.value
+
+
+def test_moe_ffn_workspace_query(L):
+    st, wb = _ffn_ws(L)
+    P = 4 * 8
+    # at least the pairs' gate/up rows, activations and down rows in fp32, on 256-byte boundaries
+    assert st == 0 and wb >= P * (2 * 2048 + 2048 + 7168) * 4 and wb % 256 == 0
+    st2, wb2 = _ffn_ws(L, t=64)
+    assert st2 == 0 and wb2 > wb
+    assert _ffn_ws(L, t=0) == (0, 0)
+    assert _ffn_ws(L, dm=7000)[0] == 2
+    assert _ffn_ws(L, t=10000)[0] == 2
+    assert _ffn_ws(L, cus=-1)[0] == 1
+    assert L.stq_moe_ffn_workspace(256, 7168, 2048, 4, 8, 256, None) == 1
+
+
+def test_moe_ffn_refuses_missing_or_small_workspace(L):
+    gs, ds = 4096 * 1176, 7168 * 336
+    _, need = _ffn_ws(L)
+
+    def f(ws, wsb):
+        return L.stq_moe_ffn_decode(FAKE, gs, FAKE, ds, 256, 7168, 2048, FAKE, 4, FAKE, FAKE, 8, FAKE, ws, wsb, None)
+    assert f(None, 0) == 1 and "workspace" in _err(L)
+    assert f(FAKE, need - 1) == 1 and str(need) in _err(L)
+    assert f(FAKE + 16, need) == 3
 
 
 def test_layer_errors_rejects_bad_arguments(L):
     le = L.stq_layer_errors
-    assert le(FAKE, FAKE, 4, 300, FAKE, 8, FAKE, FAKE, None) == 2
-    assert le(FAKE, FAKE, 4, 256, FAKE, 0, FAKE, FAKE, None) == 1
+    assert le(FAKE, FAKE, 4, 300, FAKE, 8, FAKE, FAKE, None, 0, None) == 2
+    assert le(FAKE, FAKE, 4, 256, FAKE, 0, FAKE, FAKE, None, 0, None) == 1
     assert "n_calib" in _err(L)
-    assert le(FAKE, FAKE, -1, 256, FAKE, 8, FAKE, FAKE, None) == 1
-    assert le(FAKE, None, 4, 256, FAKE, 8, FAKE, FAKE, None) == 1
-    assert le(FAKE + 4, FAKE, 4, 256, FAKE, 8, FAKE, FAKE, None) == 3
-    assert le(FAKE, FAKE, 4, 256, FAKE + 8, 8, FAKE, FAKE, None) == 3
-    assert le(FAKE, FAKE, 4, 256, FAKE, 8, FAKE + 4, FAKE, None) == 3
-    assert le(FAKE, FAKE, 4, 256, FAKE, 65536 * 64, FAKE, FAKE, None) == 2
-    assert le(None, None, 0, 256, None, 8, None, None, None) == 0   # nothing to do
+    assert le(FAKE, FAKE, -1, 256, FAKE, 8, FAKE, FAKE, None, 0, None) == 1
+    assert le(FAKE, None, 4, 256, FAKE, 8, FAKE, FAKE, None, 0, None) == 1
+    assert le(FAKE + 4, FAKE, 4, 256, FAKE, 8, FAKE, FAKE, None, 0, None) == 3
+    assert le(FAKE, FAKE, 4, 256, FAKE + 8, 8, FAKE, FAKE, None, 0, None) == 3
+    assert le(FAKE, FAKE, 4, 256, FAKE, 8, FAKE + 4, FAKE, None, 0, None) == 3
+    assert le(FAKE, FAKE, 4, 256, FAKE, 65536 * 64, FAKE, FAKE, None, 0, None) == 2
+    assert le(None, None, 0, 256, None, 8, None, None, None, 0, None) == 0   # nothing to do
+
+
+def test_layer_errors_workspace_query_and_refusal(L):
+    wb = ctypes.c_int64(-7)
+    assert L.stq_layer_errors_workspace(4096, 7168, 512, ctypes.byref(wb)) == 0
+    assert wb.value == 8 * (7168 + 2 * 8 * 4096)        # H diagonal, then 2 partials per (row, 64-row tile)
+    assert L.stq_layer_errors_workspace(0, 7168, 512, ctypes.byref(wb)) == 0 and wb.value == 0
+    assert L.stq_layer_errors_workspace(4, 300, 8, ctypes.byref(wb)) == 2
+    assert L.stq_layer_errors_workspace(4, 256, 0, ctypes.byref(wb)) == 1
+    assert L.stq_layer_errors_workspace(4, 256, 8, None) == 1
+    L.stq_layer_errors_workspace(4, 256, 8, ctypes.byref(wb))
+    need = wb.value
+    le = L.stq_layer_errors
+    assert le(FAKE, FAKE, 4, 256, FAKE, 8, FAKE, FAKE, None, 0, None) == 1 and "workspace" in _err(L)
+    assert le(FAKE, FAKE, 4, 256, FAKE, 8, FAKE, FAKE, FAKE, need - 8, None) == 1
+    assert le(FAKE, FAKE, 4, 256, FAKE, 8, FAKE, FAKE, FAKE + 8, need, None) == 3
+
+
+def test_library_allocates_no_device_memory(L):
+    """No entry point allocates or frees device memory: the library does not
+    even import HIP's allocators (workspaces are the caller's)."""
+    import shutil
+    import subprocess
+    import sparse_ternary_bit_amd as stq
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not installed")
+    out = subprocess.run([nm, "-D", "--undefined-only", stq.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    assert "hipLaunchKernel" in imported or any(n.startswith("hip") for n in imported)
+    banned = {n for n in imported if re.match(r"^hip(Ext)?(Malloc|Free|HostMalloc|HostAlloc|MallocManaged|"
+                                              r"MallocAsync|FreeAsync|MallocFromPool|MemPool)", n)}
+    assert not banned, banned
 
 
 def test_q2_roundtrip_rejects_bad_arguments(L):
