@@ -150,6 +150,25 @@ stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t
                     int64_t n_pairs, float* y, void* workspace, int64_t workspace_bytes,
                     stq_stream_t stream);
 
+/* stq_gemv for callers that cannot allocate memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, checks, plan and results as stq_gemv (bit for
+ * bit), without workspace: split outputs go to a fixed scratch array that the
+ * library holds on every GPU it runs on, STQ_GEMV_NOALLOC_SCRATCH_BYTES
+ * bytes, from the library's load until the process ends.  Shapes whose plan
+ * (stq_gemv_plan's scratch_bytes) needs more are refused with STQ_E_SHAPE
+ * before any launch.  Every call on one GPU shares that GPU's array, so calls
+ * that may run concurrently on one GPU (two streams, two host threads) race
+ * and must not overlap; nothing in the array needs to be cleared between
+ * calls (every value a call reads was written earlier in the same call).
+ * Allocates nothing; the first call on a device looks up that device's copy
+ * of the array (STQ_E_HIP if that fails). */
+#define STQ_GEMV_NOALLOC_SCRATCH_BYTES (32ll << 20)
+stq_status stq_gemv_noalloc(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts,
+                            int64_t n, int64_t k, const void* x, int x_dtype, int64_t x_row_stride,
+                            int64_t n_tokens, const int32_t* pair_expert, const int32_t* pair_token,
+                            int64_t n_pairs, float* y, stq_stream_t stream);
+
 /* The plan stq_gemv takes for these shapes (host only: no GPU work, and no
  * GPU needed when n_cus > 0), so a caller can size its workspace or check a
  * tuning override.  The three outputs are HOST

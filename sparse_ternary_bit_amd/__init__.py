@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "QK", "BLOCK_BYTES", "ENC_WLS", "ENC_AMAX", "StqError", "lib", "lib_path",
-    "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "gemv_plan", "grouped_gemm", "moe_ffn_decode",
+    "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "gemv_noalloc", "gemv_plan", "grouped_gemm",
+    "moe_ffn_decode",
     "moe_ffn_workspace", "layer_errors", "layer_errors_workspace", "q2_roundtrip", "greedy_allocation",
     "stream_read_probe",
 ]
@@ -67,6 +68,9 @@ def lib() -> ctypes.CDLL:
     L.stq_gemv.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_i64, _c_i64,
                            _c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]
     L.stq_gemv.restype = _c_int
+    L.stq_gemv_noalloc.argtypes = [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_i64, _c_i64,
+                                   _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]
+    L.stq_gemv_noalloc.restype = _c_int
     L.stq_gemv_plan.argtypes = [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(_c_i64)]
     L.stq_gemv_plan.restype = _c_int
@@ -244,6 +248,34 @@ def gemv(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: int, k: i
                                       x.data_ptr(), xd, x_stride, n_tokens, _ptr(pair_expert),
                                       _ptr(pair_token), int(n_pairs), out.data_ptr(), *_ws_args(workspace),
                                       _stream()))
+    return out
+
+
+def gemv_noalloc(w_table: torch.Tensor, expert_stride: int, n_experts: int, n: int, k: int, x: torch.Tensor,
+                 pair_expert: torch.Tensor | None, pair_token: torch.Tensor | None, out: torch.Tensor) -> torch.Tensor:
+    """gemv without any allocation (neither here nor in the library): the caller passes `out`
+    [n_pairs, n] fp32; split outputs use the library's fixed per-GPU scratch, so calls on one
+    GPU must not overlap.  Shapes needing more scratch than it holds raise."""
+    _on_gpu("w_table", w_table, torch.uint8)
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be float32 or bfloat16")
+    _on_gpu("x", x, x.dtype)
+    _on_gpu("out", out, torch.float32)
+    n_tokens = x.shape[0]
+    n_pairs = out.shape[0]
+    for nm, t in (("pair_expert", pair_expert), ("pair_token", pair_token)):
+        if t is not None:
+            _on_gpu(nm, t, torch.int32)
+            if t.numel() != n_pairs:
+                raise ValueError(f"{nm} must hold out.shape[0] entries")
+    _holds("out", out, int(n_pairs) * int(n))
+    if int(n_pairs) > 0:
+        _table("w_table", w_table, n_experts, expert_stride, n, k)
+    x_stride = x.stride(0) if n_tokens > 1 else x.shape[1]
+    _check("stq_gemv_noalloc",
+           lib().stq_gemv_noalloc(w_table.data_ptr(), int(expert_stride), int(n_experts), int(n), int(k),
+                                  x.data_ptr(), X_BF16 if x.dtype == torch.bfloat16 else X_F32, x_stride, n_tokens,
+                                  _ptr(pair_expert), _ptr(pair_token), int(n_pairs), out.data_ptr(), _stream()))
     return out
 
 

@@ -4,9 +4,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -103,30 +105,50 @@ stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, floa
   return ok();
 }
 
+namespace {
+
+// Argument checks of stq_gemv and stq_gemv_noalloc; `nothing` is set when
+// the call has no work (no pairs or no rows), which is not an error.
+stq_status gemv_check(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts, int64_t n, int64_t k,
+                      const void* x, int x_dtype, int64_t x_row_stride, int64_t n_tokens, const int32_t* pair_expert,
+                      const int32_t* pair_token, int64_t n_pairs, const float* y, const char* who, bool* nothing) {
+  *nothing = false;
+  if (n_experts < 1 || n < 0 || n_tokens < 0 || n_pairs < 0) return fail(STQ_E_ARG, "%s: negative count or no experts", who);
+  if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "%s: k=%lld is not a positive multiple of 256", who, (long long)k);
+  if (x_dtype != STQ_X_F32 && x_dtype != STQ_X_BF16) return fail(STQ_E_ARG, "%s: unknown x_dtype %d", who, x_dtype);
+  if (n > INT_MAX || n_tokens > INT_MAX || n_experts > INT_MAX) return fail(STQ_E_SHAPE, "%s: count exceeds int32", who);
+  if (n_pairs > 65535) return fail(STQ_E_SHAPE, "%s: more than 65535 pairs in one call", who);
+  const int64_t rb = stq_row_bytes(k);
+  if (expert_stride_bytes < n * rb) return fail(STQ_E_SHAPE, "%s: expert stride %lld < n*row_bytes %lld", who, (long long)expert_stride_bytes, (long long)(n * rb));
+  if (x_row_stride < k) return fail(STQ_E_SHAPE, "%s: x_row_stride < k", who);
+  if (n_pairs == 0 || n == 0) {
+    *nothing = true;
+    return STQ_OK;
+  }
+  if (!w_table || !x || !y) return fail(STQ_E_ARG, "%s: null pointer", who);
+  if (!aligned(w_table, 16) || expert_stride_bytes % 16) return fail(STQ_E_ALIGN, "%s: w_table / expert stride not 16-byte aligned", who);
+  if (!aligned(x, 4) || !aligned(y, 4) || !aligned(pair_expert, 4) || !aligned(pair_token, 4)) return fail(STQ_E_ALIGN, "%s: x, y or pair arrays not 4-byte aligned", who);
+  if (x_dtype == STQ_X_BF16 && (x_row_stride % 2)) return fail(STQ_E_ALIGN, "%s: bf16 x_row_stride must be even", who);
+  return STQ_OK;
+}
+
+}  // namespace
+
 stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts, int64_t n, int64_t k,
                     const void* x, int x_dtype, int64_t x_row_stride, int64_t n_tokens,
                     const int32_t* pair_expert, const int32_t* pair_token, int64_t n_pairs, float* y,
                     void* workspace, int64_t workspace_bytes, stq_stream_t stream) {
-  if (n_experts < 1 || n < 0 || n_tokens < 0 || n_pairs < 0) return fail(STQ_E_ARG, "stq_gemv: negative count or no experts");
-  if (k <= 0 || k % STQ_QK) return fail(STQ_E_SHAPE, "stq_gemv: k=%lld is not a positive multiple of 256", (long long)k);
-  if (x_dtype != STQ_X_F32 && x_dtype != STQ_X_BF16) return fail(STQ_E_ARG, "stq_gemv: unknown x_dtype %d", x_dtype);
-  if (n > INT_MAX || n_tokens > INT_MAX || n_experts > INT_MAX) return fail(STQ_E_SHAPE, "stq_gemv: count exceeds int32");
-  if (n_pairs > 65535) return fail(STQ_E_SHAPE, "stq_gemv: more than 65535 pairs in one call");
-  const int64_t rb = stq_row_bytes(k);
-  if (expert_stride_bytes < n * rb) return fail(STQ_E_SHAPE, "stq_gemv: expert stride %lld < n*row_bytes %lld", (long long)expert_stride_bytes, (long long)(n * rb));
-  if (x_row_stride < k) return fail(STQ_E_SHAPE, "stq_gemv: x_row_stride < k");
+  bool nothing = false;
+  stq_status st = gemv_check(w_table, expert_stride_bytes, n_experts, n, k, x, x_dtype, x_row_stride, n_tokens,
+                             pair_expert, pair_token, n_pairs, y, "stq_gemv", &nothing);
+  if (st != STQ_OK) return st;
   if (workspace_bytes < 0) return fail(STQ_E_ARG, "stq_gemv: workspace_bytes < 0");
-  if (n_pairs == 0 || n == 0) return ok();
-  if (!w_table || !x || !y) return fail(STQ_E_ARG, "stq_gemv: null pointer");
-  if (!aligned(w_table, 16) || expert_stride_bytes % 16) return fail(STQ_E_ALIGN, "stq_gemv: w_table / expert stride not 16-byte aligned");
-  if (!aligned(x, 4) || !aligned(y, 4) || !aligned(pair_expert, 4) || !aligned(pair_token, 4)) return fail(STQ_E_ALIGN, "stq_gemv: x, y or pair arrays not 4-byte aligned");
-  if (x_dtype == STQ_X_BF16 && (x_row_stride % 2)) return fail(STQ_E_ALIGN, "stq_gemv: bf16 x_row_stride must be even");
-
+  if (nothing) return ok();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   stq::GemvArgs ga{w_table, expert_stride_bytes, n_experts, n, k, x, x_dtype == STQ_X_BF16 ? 1 : 0,
                    x_row_stride, n_tokens, pair_expert, pair_token, n_pairs, y, 1};
   const stq::GemvPlan pl = stq::plan_gemv(ga, stq::cus_of_stream(s));
-  const stq_status st = check_workspace(workspace, workspace_bytes, pl.partial_bytes, "stq_gemv");
+  st = check_workspace(workspace, workspace_bytes, pl.partial_bytes, "stq_gemv");
   if (st != STQ_OK) return st;
   hipError_t le = stq::launch_gemv(ga, pl, workspace, s);
   if (le != hipSuccess) return hip_fail(le, "stq_gemv launch");
@@ -365,6 +387,82 @@ stq_status stq_stream_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
   if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(STQ_E_ALIGN, "stq_stream_read_probe: buf must be 16-byte and sink 4-byte aligned");
   hipError_t e = stq::launch_stream_read(buf, bytes, sink, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "stq_stream_read_probe launch");
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// stq_gemv_noalloc: stq_gemv for callers that cannot allocate.  Its split
+// outputs live in `scratch`, a fixed array of device memory in the library
+// itself (each GPU holds its own copy from the library's load until the
+// process ends).  In host code `scratch` names a host-side stand-in, so the
+// device address of each GPU's copy is looked up once per device with that
+// device current and kept; only that address reaches a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kNoAllocScratchBytes = STQ_GEMV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+stq_status scratch_for_stream(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(s, &dev);
+  if (e != hipSuccess) return hip_fail(e, "stq_gemv_noalloc: device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(STQ_E_HIP, "stq_gemv_noalloc: device %d out of range", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = -1;
+      e = hipGetDevice(&cur);
+      if (e != hipSuccess) return hip_fail(e, "stq_gemv_noalloc: current device");
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "stq_gemv_noalloc: set device");
+      void* q = nullptr;
+      e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+      if (e != hipSuccess) return hip_fail(e, "stq_gemv_noalloc: scratch address");
+      if (back != hipSuccess) return hip_fail(back, "stq_gemv_noalloc: restore device");
+      if (!q || !aligned(q, 256)) return fail(STQ_E_HIP, "stq_gemv_noalloc: scratch address unusable");
+      g_scratch_ptr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return STQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+stq_status stq_gemv_noalloc(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts, int64_t n,
+                            int64_t k, const void* x, int x_dtype, int64_t x_row_stride, int64_t n_tokens,
+                            const int32_t* pair_expert, const int32_t* pair_token, int64_t n_pairs, float* y,
+                            stq_stream_t stream) {
+  bool nothing = false;
+  stq_status st = gemv_check(w_table, expert_stride_bytes, n_experts, n, k, x, x_dtype, x_row_stride, n_tokens,
+                             pair_expert, pair_token, n_pairs, y, "stq_gemv_noalloc", &nothing);
+  if (st != STQ_OK || nothing) return st == STQ_OK ? ok() : st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  stq::GemvArgs ga{w_table, expert_stride_bytes, n_experts, n, k, x, x_dtype == STQ_X_BF16 ? 1 : 0,
+                   x_row_stride, n_tokens, pair_expert, pair_token, n_pairs, y, 1};
+  const stq::GemvPlan pl = stq::plan_gemv(ga, stq::cus_of_stream(s));
+  if (pl.partial_bytes > kNoAllocScratchBytes)
+    return fail(STQ_E_SHAPE, "stq_gemv_noalloc: these shapes need %lld bytes of scratch, more than the %lld it holds",
+                (long long)pl.partial_bytes, (long long)kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (pl.partial_bytes > 0) {
+    st = scratch_for_stream(s, &ws);
+    if (st != STQ_OK) return st;
+  }
+  hipError_t le = stq::launch_gemv(ga, pl, ws, s);
+  if (le != hipSuccess) return hip_fail(le, "stq_gemv_noalloc launch");
   return ok();
 }
 

@@ -385,3 +385,23 @@ def test_stream_read_probe_rejects_bad_arguments(L):
     assert L.stq_stream_read_probe(None, 64, FAKE, None) == 1
     assert L.stq_stream_read_probe(FAKE + 8, 64, FAKE, None) == 3
     assert L.stq_stream_read_probe(None, 0, None, None) == 0
+
+
+def test_gemv_noalloc_checks_and_refuses_shapes_beyond_its_scratch(L, monkeypatch):
+    """stq_gemv_noalloc checks its arguments like stq_gemv and refuses, before
+    touching the GPU, shapes whose plan needs more than its fixed scratch."""
+    f = L.stq_gemv_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    n, k, E, P = 4096, 7168, 2, 4096
+    args = lambda **kw: [kw.get("w", FAKE), n * 1176, E, n, kw.get("k", k), FAKE, 1, k, P, None, None,
+                         kw.get("np_", P), kw.get("y", FAKE), None]
+    assert f(*args(k=1000)) == 2
+    assert f(*args(y=None)) == 1
+    assert f(*args(w=FAKE + 8)) == 3
+    assert f(*args(np_=0, w=None, y=None)) == 0
+    monkeypatch.setenv("STQ_GEMV_PLAN", "16,8")          # 128 slots of 4096 x 4096 fp32 partial sums
+    assert _plan(L, ne=E, np_=P)[1][2] > 32 << 20
+    assert f(*args()) == 2 and "scratch" in _err(L)
