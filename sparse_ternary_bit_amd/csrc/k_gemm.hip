@@ -9,34 +9,38 @@
 // bf16 product is exact in fp32; sums are fp32, and each 256-weight block's
 // partial sum is scaled by its fp32(d) once (one FMA per output per block).
 //
-// Work unit: a workgroup of 8 wavefronts owns 512 weight rows (one 64-row
+// Work unit: a workgroup of 4 wavefronts owns 256 weight rows (one 64-row
 // tile of the packed matrix per wavefront) of one expert and all of that
 // expert's tokens, in passes of at most 80 tokens (5 tiles of 16).  Every
 // weight is therefore decoded once per pass, and each decoded MFMA operand
-// is reused for every token tile of the pass.
+// is reused for every token tile of the pass.  Two workgroups share a CU
+// (about 69 KB of LDS and 256 VGPRs per wavefront each), so the barriers and
+// block boundaries of one overlap the other's matrix-core work.
 //
 // Per 256-weight block b:
-//   * activations of block b+1 for the pass stream from global memory
-//     straight into LDS (16-byte direct loads) into the second of two
-//     buffers; a token's 32 16-byte chunks are stored XOR-swizzled by the
-//     token index (mod 16) so the matrix-operand reads below are
-//     bank-conflict free;
+//   * activations stream from global memory straight into LDS (16-byte
+//     direct loads) half a block (128 per token) at a time into the second
+//     of two buffers while the other half is multiplied; a token's 16
+//     16-byte chunks of a half are stored XOR-swizzled by the token index
+//     (mod 16) so the matrix-operand reads below are bank-conflict free;
 //   * each wavefront's contiguous tile run of block b+1 streams into LDS the
 //     same way; each lane then reads its own row's 42-byte block there,
 //     realigns it and turns it into four 16-byte records, one per MFMA
-//     k-quarter: for each of
-//     the block's 8 k-steps the quarter's two group codes, pre-scaled by 4 so
-//     a code is directly a byte offset into the pattern table;
-//   * per k-step an MFMA lane reads its four row tiles' record words (one
-//     16-byte read; a word serves two k-steps), and per row tile extracts
-//     two codes (two bit-field extracts) and reads the bf16 lanes of both
-//     patterns from a 32-entry table in LDS (two 8-byte reads): that is the
-//     whole weight decode;
+//     k-quarter: for each of the block's 8 k-steps the quarter's two group
+//     codes, pre-scaled by 4 so a code is directly a byte offset into the
+//     pattern table;
+//   * per half block an MFMA lane reads its four row tiles' record words for
+//     the half's 4 k-steps (two 16-byte reads), and per k-step and row tile
+//     extracts two codes (two bit-field extracts) and reads the bf16 lanes
+//     of both patterns from a 32-entry table in LDS (two 8-byte reads): that
+//     is the whole weight decode.  The k-steps are software-pipelined: step
+//     s+1's operand reads are issued before step s's MFMAs;
 //   * after the block's 8 k-steps the fp32 partial sums are scaled by the
 //     rows' d into the fp32 totals.
-// One barrier per block.  Workgroups of one expert are launched on the same
-// XCD (workgroup ids are dealt to the 8 XCDs round robin), so the expert's
-// activations are fetched once into that XCD's L2 and shared by its 8 slabs.
+// Two barriers per block (one per half).  Workgroups of one expert are
+// launched on the same XCD (workgroup ids are dealt to the 8 XCDs round
+// robin), so the expert's activations are fetched once into that XCD's L2
+// and shared by its 16 slabs.
 #include "stq_device.hpp"
 #include "stq_launch.hpp"
 
@@ -47,13 +51,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kSlab = kWaves * kTileRows;   // 512 weight rows per workgroup
+constexpr int kSlab = kWaves * kTileRows;   // 256 weight rows per workgroup
 constexpr int kMaxTiles = 5;                // token tiles of 16 per pass
 constexpr int kMaxTok = kMaxTiles * 16;     // 80 tokens per pass
-constexpr int kRowBytes = kQK * 2;          // one token's 256 activations
-constexpr int kXBuf = kMaxTok * kRowBytes;  // 40960 bytes per buffer
+constexpr int kHalfBytes = kQK;             // one token's 128 activations: half a block
+constexpr int kXBuf = kMaxTok * kHalfBytes; // 20480 bytes per buffer
 constexpr int kXcds = 8;
 constexpr int kWRaw = 3 * 1024;             // 16-byte aligned window over one 2688-byte tile run
 
@@ -84,7 +88,7 @@ struct Smem {
   // (the writers, a row tile per 16 lanes, meet 2-way bank conflicts on
   // their 4-byte stores, which cost less than the 4-byte reads they replace)
   alignas(16) uint32_t rec[kWaves][4][4][16][4];
-  alignas(16) char x[2][kXBuf];           // activations, current and next block
+  alignas(16) char x[2][kXBuf];           // activations, current and next half block
   alignas(16) char wraw[kWaves][kWRaw];   // each wavefront's tile run of the next block
 };
 
@@ -111,16 +115,17 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
   const uint8_t* tb = wexp + static_cast<int64_t>(min(trow0, a.n)) * a.nb * kBlockBytes;
   const Rsrc rs = make_rsrc(tb, (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u);
 
-  // activations: 2 tokens (64 chunks of 16 bytes) per wavefront instruction;
-  // chunk c of token t goes to slot c ^ (t & 15) of the token's 512 bytes
-  const int n_ins = (mt + 1) >> 1;
+  // activations, half a block (128 of them, 16 chunks of 16 bytes) per token
+  // at a time: 4 tokens per wavefront instruction; chunk c of token t goes to
+  // slot c ^ (t & 15) of the token's 256 bytes
+  const int n_ins = (mt + 3) >> 2;
   const uint32_t xrow = static_cast<uint32_t>(a.k) * 2;
   const Rsrc xs_rs = make_rsrc(a.x + row0 * a.k, static_cast<uint32_t>(mt) * xrow);
-  auto stage_x = [&](int b, int buf) {
+  auto stage_x = [&](int h, int buf) {
     for (int j = wave; j < n_ins; j += kWaves) {
-      const int t = 2 * j + (lane >> 5);
-      const int c = (lane & 31) ^ (t & 15);
-      const uint32_t voff = static_cast<uint32_t>(min(t, mt - 1)) * xrow + static_cast<uint32_t>(b) * kRowBytes + c * 16;
+      const int t = 4 * j + (lane >> 4);
+      const int c = (lane & 15) ^ (t & 15);
+      const uint32_t voff = static_cast<uint32_t>(min(t, mt - 1)) * xrow + static_cast<uint32_t>(h) * kHalfBytes + c * 16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xs_rs, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(sh.x[buf] + j * 1024)),
           16, static_cast<int>(voff), 0, 0, 0);
@@ -175,12 +180,12 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
   };
 
 
-  // B operand addresses: token 16*bt + r, chunk 4s + q in slot (4s + q) ^ r,
-  // which is ((4 * (s & 3)) ^ q ^ r) + 16 * (s >> 2)
+  // B operand addresses: token 16*bt + r, chunk 4s + q of its half block
+  // (s the k-step within the half) in slot (4s + q) ^ r = (4s) ^ q ^ r
   const int u = q ^ r;
   int xb[4];
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) xb[s4] = r * kRowBytes + ((4 * s4) ^ u) * 16;
+  for (int s4 = 0; s4 < 4; ++s4) xb[s4] = r * kHalfBytes + ((4 * s4) ^ u) * 16;
 
   const f32x4_t zero4 = {opaque_zero(), opaque_zero(), opaque_zero(), opaque_zero()};
   f32x4_t tot[4][NT];
@@ -189,67 +194,97 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
 #pragma unroll
     for (int t = 0; t < NT; ++t) tot[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: block 0
+  // prologue: block 0 (its first half of activations, its weights)
   stage_x(0, 0);
   stage_w(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads have landed
   make_records(block_from_window(0));
   __syncthreads();
 
-  for (int b = 0; b < a.nb; ++b) {
-    const int buf = b & 1;
-    const bool more = b + 1 < a.nb;
-    if (more) {
-      stage_x(b + 1, buf ^ 1);
-      stage_w(b + 1);
-    }
-    const char* xs = sh.x[buf];
+  // operands of k-step s: A[i] (row tile i) from the two group codes of the
+  // record word for this k-step pair, B[t] (token tile t) from the activations
+  auto decode_a = [&](const u32x4_t& Rw, int s, bf16x8_t (&A)[4]) {
     const char* lut = reinterpret_cast<const char*>(sh.lut);
-
-    f32x4_t part[4][NT];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      bf16x8_t A[4];
-      const u32x4_t Rw = *reinterpret_cast<const u32x4_t*>(&sh.rec[wave][s >> 1][q][r][0]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = Rw[i];
-        const uint32_t c1 = __builtin_amdgcn_ubfe(w, 16 * (s & 1), 8);
-        const uint32_t c2 = __builtin_amdgcn_ubfe(w, 16 * (s & 1) + 8, 8);
-        u32x4_t v;
-        v[0] = *reinterpret_cast<const uint32_t*>(lut + c1);
-        v[1] = *reinterpret_cast<const uint32_t*>(lut + c1 + 128);
-        v[2] = *reinterpret_cast<const uint32_t*>(lut + c2);
-        v[3] = *reinterpret_cast<const uint32_t*>(lut + c2 + 128);
-        A[i] = __builtin_bit_cast(bf16x8_t, v);
-      }
-      const int xo = xb[s & 3] + 256 * (s >> 2);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(xs + xo + t * 16 * kRowBytes);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4_t c = (s == 0) ? zero4 : part[i][t];
-          part[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], B, c, 0, 0, 0);
-        }
-      }
-      // keep each k-step's operand reads next to its MFMAs (bounded live ranges)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // scale the block's partial sums: rows 16i + 4q + j of the tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sh.dsc[wave][16 * i + 4 * q]);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tot[i][t][j] = fmaf(d4[j], part[i][t][j], tot[i][t][j]);
+      const uint32_t w = Rw[i];
+      const uint32_t c1 = __builtin_amdgcn_ubfe(w, 16 * (s & 1), 8);
+      const uint32_t c2 = __builtin_amdgcn_ubfe(w, 16 * (s & 1) + 8, 8);
+      u32x4_t v;
+      v[0] = *reinterpret_cast<const uint32_t*>(lut + c1);
+      v[1] = *reinterpret_cast<const uint32_t*>(lut + c1 + 128);
+      v[2] = *reinterpret_cast<const uint32_t*>(lut + c2);
+      v[3] = *reinterpret_cast<const uint32_t*>(lut + c2 + 128);
+      A[i] = __builtin_bit_cast(bf16x8_t, v);
     }
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // block b+1's weights and activations are in LDS
-      make_records(block_from_window(b + 1));
+  };
+  auto read_b = [&](const char* xs, int s, bf16x8_t (&B)[NT]) {
+    const int xo = xb[s & 3];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) B[t] = *reinterpret_cast<const bf16x8_t*>(xs + xo + t * 16 * kHalfBytes);
+  };
+
+  for (int b = 0; b < a.nb; ++b) {
+    const bool more = b + 1 < a.nb;
+    // The block's four record words (one per k-step pair) and, per half
+    // block, a software pipeline over its 4 k-steps: the operands of step
+    // s + 1 are read from LDS before the MFMAs of step s are issued.
+    bf16x8_t A[2][4], Bv[2][NT];
+    f32x4_t part[4][NT];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int h = 2 * b + half;
+      const int buf = h & 1;
+      // the next half block's activations (and, in the first half, the next
+      // block's weights) stream into LDS while this half is multiplied
+      if (half == 0 || more) stage_x(h + 1, buf ^ 1);
+      if (half == 0 && more) stage_w(b + 1);
+      const char* xs = sh.x[buf];
+      // this half's two record words (k-step pairs 2 half, 2 half + 1)
+      u32x4_t R[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        R[s2] = *reinterpret_cast<const u32x4_t*>(&sh.rec[wave][2 * half + s2][q][r][0]);
+      decode_a(R[0], 4 * half, A[0]);
+      read_b(xs, 0, Bv[0]);
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int s = 4 * half + sl;
+        const int cur = sl & 1;
+        if (sl + 1 < 4) {
+          decode_a(R[(sl + 1) >> 1], s + 1, A[cur ^ 1]);
+          read_b(xs, sl + 1, Bv[cur ^ 1]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4_t c = (s == 0) ? zero4 : part[i][t];
+            part[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[cur][i], Bv[cur][t], c, 0, 0, 0);
+          }
+        }
+        // keep each step's reads (for the next step) and MFMAs together
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (half == 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's share of the second half is in LDS
+      } else {
+        // scale the block's partial sums: rows 16i + 4q + j of the tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sh.dsc[wave][16 * i + 4 * q]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tot[i][t][j] = fmaf(d4[j], part[i][t][j], tot[i][t][j]);
+        }
+        if (more) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // block b+1's weights and first activations are in LDS
+          make_records(block_from_window(b + 1));
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // y[row0 + 16t + r, trow0 + 16i + 4q + j]
@@ -272,7 +307,9 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
   }
 }
 
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GArgs a) {
+// Two workgroups per CU (LDS ~69 KB each, 256 VGPRs per wavefront), so one
+// workgroup's barriers and block boundaries overlap the other's MFMAs.
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GArgs a) {
   __shared__ Smem sh;
   // workgroup -> (expert, slab): the slabs of one expert share an XCD
   const int wg = blockIdx.x;
