@@ -89,10 +89,18 @@ struct KArgs {
   int ppt;         // without pair_token: pair q uses token q / ppt
 };
 
+// bf16 passes of at least this many tokens run on the matrix cores (in the
+// kernel variant that has that form; fewer tokens use the tables)
+constexpr int kMfmaMinTokens = 3;
+
 __device__ __forceinline__ int pair_expert(const KArgs& a, int q) { return a.pe ? a.pe[q] : 0; }
 __device__ __forceinline__ int pair_token(const KArgs& a, int q) { return a.pt ? a.pt[q] : q / a.ppt; }
 
 struct Shared {
+  // bf16 pattern table of the matrix-core form: entry c of lut[0..31] holds
+  // lanes 0,1 of code c, entry c of lut[32..63] lanes 2,3 (two 4-byte reads
+  // 128 bytes apart are bank-conflict free whatever the codes)
+  uint32_t lut[64];
   alignas(16) char tab[2][kBufBytes];       // two table buffers; per token 32 signed sums x 64 groups
   int pairs[kMT];
   int toks[kMT];
@@ -310,28 +318,26 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // Table items of this thread.  Pair tables (MC = 2 or 4):
-  // item (token pair tid / 256, group g, zero lane z), one per thread.  Else
-  // item i = 256*m + 4*g + z for token m, items tid and tid + 512.
+  // Table items of this thread.  Pair tables (MC = 2 or 4): item (token pair
+  // tid / 256, group g, zero lane z).  One token (MC = 1): item (g, z) of the
+  // token, threads 0..255.
   constexpr bool kPair = MC >= 2;
-  static_assert(!kPair || MC == 2 || MC == 4, "pair tables take 2 or 4 tokens");
-  constexpr int kItems = kPair ? 128 * MC : 256 * MC;
+  static_assert(MC == 1 || MC == 2 || MC == 4, "one-token tables or pair tables of 2 or 4 tokens");
+  constexpr int kItems = kPair ? 128 * MC : 256;
   const int it_g = (tid >> 2) & 63, it_z = tid & 3;
-  const int m0 = tid >> 8, m1 = m0 + 2;
-  const bool has0 = tid < kItems, has1 = !kPair && tid + kRows < kItems;
+  const int m0 = tid >> 8;
+  const bool has0 = tid < kItems;
   int tok[MC];
 #pragma unroll
   for (int m = 0; m < MC; ++m) tok[m] = __builtin_amdgcn_readfirstlane(sh.toks[m]);
-  // single tables: tok0 / tok1 are the tokens of items tid / tid + 512;
-  // pair tables: the two tokens of this thread's pair
+  // the token (one-token tables) or the two tokens of this thread's pair
   int tok0 = 0, tok1 = 0;
 #pragma unroll
   for (int m = 0; m < MC; ++m) {
-    if (kPair ? m == 2 * m0 : m == m0) tok0 = tok[m];
-    if (kPair ? m == 2 * m0 + 1 : m == m1) tok1 = tok[m];
+    if (kPair ? m == 2 * m0 : m == 0) tok0 = tok[m];
+    if (kPair && m == 2 * m0 + 1) tok1 = tok[m];
   }
-  const int tab_off0 = kPair ? m0 * kPairStride + it_g * 256 + it_z * 64 : m0 * kTokStride + it_g * 128 + it_z * 32;
-  const int tab_off1 = m1 * kTokStride + it_g * 128 + it_z * 32;
+  const int tab_off0 = kPair ? m0 * kPairStride + it_g * 256 + it_z * 64 : it_g * 128 + it_z * 32;
 
 #pragma unroll
   for (int m = 0; m < kMT; ++m) acc[m] = 0.0f;
@@ -350,14 +356,12 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
       x[0].load(a, tok0, col);
       if (kPair) x[1].load(a, tok1, col);
     }
-    if (has1) x[1].load(a, tok1, col);
   };
   auto build = [&](const XGroup<kMode> (&x)[2], char* t) {
     if constexpr (kPair) {
       if (has0) build_pair_entries<kMode>(x[0], x[1], it_z, t + tab_off0);
     } else {
       if (has0) build_entries<kMode>(x[0], it_z, t + tab_off0);
-      if (has1) build_entries<kMode>(x[1], it_z, t + tab_off1);
     }
   };
   // 42*(b*valid + lane) is 2 mod 4 exactly when b*valid + lane is odd
@@ -388,6 +392,149 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
     if (b_begin + 1 < b_end) load_x(xb, b_begin + 1);
     if (b_begin + 2 < b_end) load_x(xa, b_begin + 2);
     build(x0, buf0);
+    __syncthreads();
+  }
+  for (int b = b_begin; b < b_end; b += 2) {
+    step(wa, xb, buf0, buf1, b);
+    if (b + 1 < b_end) step(wb, xa, buf1, buf0, b + 1);
+  }
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// One block of this thread's row for the pass's four tokens on the matrix
+// cores.  v_mfma_f32_4x4x4_16b_bf16 multiplies 16 independent 4x4 blocks;
+// here block b is the wavefront's row quad 4b..4b+3 and k is one group: the B
+// operand of lane l is row l's four weights of the group (a pattern read
+// from the bf16 table), the A operand is the group's four activations of
+// tokens 0..3, which the instruction broadcasts from one block to all 16
+// (cbsz 4, abid): lane 4b+i holds token i's activations of group 16s+b for
+// s = 0..3, so four 8-byte reads per block fetch all 64 groups.  Lane l's
+// four results are row l for tokens 0..3.  Products of bf16 values are exact
+// in fp32; the group sums accumulate in fp32 (even and odd groups apart),
+// then the block's d scales them (one FMA per token), as in block_dot.
+// Group G's product: the activations of group G (block G % 16 of the set
+// G / 16) broadcast to all 16 blocks.  abid must be an immediate, hence the
+// template.
+template <int G>
+__device__ __forceinline__ f32x4_t mfma_group(const s16x4_t (&xa)[4], s16x4_t w, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xa[G >> 4], w, c, 4, G & 15, 0);
+}
+
+// Code word W (groups 8W..8W+7) of one block: pattern reads, then the MFMAs
+// of the four low-nibble groups into c0 and the four high-nibble ones into c1.
+template <int W>
+__device__ __forceinline__ void word_mfma(const Block& blk, const char* lb, const s16x4_t (&xa)[4], f32x4_t& c0,
+                                          f32x4_t& c1) {
+  const uint32_t Q = blk.qs[W];
+  const uint32_t Hs = blk.qh[W >> 2] << (6 - 2 * (W & 3));
+  // byte j of cl / cu = 4 * code of group 8W+j / 8W+4+j
+  uint32_t cl = ((Q << 2) & 0x3C3C3C3Cu) | (Hs & 0x40404040u);
+  uint32_t cu = ((Q >> 2) & 0x3C3C3C3Cu) | ((Hs >> 1) & 0x40404040u);
+  asm("" : "+v"(cl), "+v"(cu));  // one bit-field extract per code, as in block_dot
+  s16x4_t bl[4], bu[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t ol = __builtin_amdgcn_ubfe(cl, 8 * j, 8);
+    const uint32_t ou = __builtin_amdgcn_ubfe(cu, 8 * j, 8);
+    const uint64_t l0 = *reinterpret_cast<const uint32_t*>(lb + ol);
+    const uint64_t l1 = *reinterpret_cast<const uint32_t*>(lb + ol + 128);
+    const uint64_t u0 = *reinterpret_cast<const uint32_t*>(lb + ou);
+    const uint64_t u1 = *reinterpret_cast<const uint32_t*>(lb + ou + 128);
+    bl[j] = __builtin_bit_cast(s16x4_t, (l1 << 32) | l0);
+    bu[j] = __builtin_bit_cast(s16x4_t, (u1 << 32) | u0);
+  }
+  c0 = mfma_group<8 * W + 0>(xa, bl[0], c0);
+  c1 = mfma_group<8 * W + 4>(xa, bu[0], c1);
+  c0 = mfma_group<8 * W + 1>(xa, bl[1], c0);
+  c1 = mfma_group<8 * W + 5>(xa, bu[1], c1);
+  c0 = mfma_group<8 * W + 2>(xa, bl[2], c0);
+  c1 = mfma_group<8 * W + 6>(xa, bu[2], c1);
+  c0 = mfma_group<8 * W + 3>(xa, bl[3], c0);
+  c1 = mfma_group<8 * W + 7>(xa, bu[3], c1);
+}
+
+__device__ __forceinline__ void block_mfma(const char* xs, const uint32_t* lut, const Block& blk, int lane,
+                                           float (&acc)[kMT]) {
+  const float d = half_bits_to_float(blk.d16);
+  s16x4_t xa[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const s16x4_t*>(xs + (64 * s + lane) * 8);
+  f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  const char* lb = reinterpret_cast<const char*>(lut);
+  word_mfma<0>(blk, lb, xa, c0, c1);
+  word_mfma<1>(blk, lb, xa, c0, c1);
+  word_mfma<2>(blk, lb, xa, c0, c1);
+  word_mfma<3>(blk, lb, xa, c0, c1);
+  word_mfma<4>(blk, lb, xa, c0, c1);
+  word_mfma<5>(blk, lb, xa, c0, c1);
+  word_mfma<6>(blk, lb, xa, c0, c1);
+  word_mfma<7>(blk, lb, xa, c0, c1);
+#pragma unroll
+  for (int m = 0; m < kMT; ++m) acc[m] = fmaf(d, c0[m] + c1[m], acc[m]);
+}
+
+// Blocks [b_begin, b_end) of this workgroup's rows for bf16 activations and
+// up to four tokens on the matrix cores (token slots past the pass's count
+// repeat its last token; their results are not stored).  The pipeline is
+// run_chunk's: weights two blocks ahead, activations three; each block's
+// activations (4 tokens x 64 groups x 8 bytes) are staged in LDS in
+// [group][token] order while the previous block is multiplied.
+__device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const uint8_t* wexp, int b_begin,
+                                               int b_end, float (&acc)[kMT]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // staging item of this thread (threads 0..255): token tid >> 6, group tid & 63
+  const int st_m = tid >> 6, st_g = tid & 63;
+  const bool stages = tid < 4 * 64;
+  int tok_st = 0;
+#pragma unroll
+  for (int m = 0; m < kMT; ++m) {
+    const int t = __builtin_amdgcn_readfirstlane(sh.toks[m]);
+    if (m == st_m) tok_st = t;
+  }
+  const int st_off = (st_g * 4 + st_m) * 8;
+
+#pragma unroll
+  for (int m = 0; m < kMT; ++m) acc[m] = 0.0f;
+
+  const int rowbase = blockIdx.x * kRows + wave * 64;
+  const int valid = max(0, min(kTileRows, a.n - rowbase));
+  const uint8_t* tb = wexp + static_cast<int64_t>(min(rowbase, a.n)) * a.nb * kBlockBytes;
+  const Rsrc rs = make_rsrc(tb, (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u);
+  auto load_w = [&](RawBlock& r, int b) {
+    load_raw_block(rs, (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes, r);
+  };
+  auto load_x = [&](XGroup<kXBF16>& x, int b) {
+    if (stages) x.load(a, tok_st, static_cast<int64_t>(b) * kQK + 4 * st_g);
+  };
+  auto stage = [&](const XGroup<kXBF16>& x, char* t) {
+    if (stages) *reinterpret_cast<uint2*>(t + st_off) = make_uint2(x.v[0], x.v[1]);
+  };
+  const bool lane_odd = (lane & 1) != 0;
+  char* buf0 = sh.tab[0];
+  char* buf1 = sh.tab[1];
+
+  RawBlock wa, wb;
+  XGroup<kXBF16> xa, xb;
+  auto step = [&](RawBlock& wcur, XGroup<kXBF16>& xnext, char* tcur, char* tnext, int b) {
+    const bool odd = ((static_cast<uint32_t>(b) * valid) & 1u) ? !lane_odd : lane_odd;
+    const Block blk = realign_block(wcur, odd);
+    if (b + 1 < b_end) stage(xnext, tnext);
+    if (b + 2 < b_end) load_w(wcur, b + 2);
+    if (b + 3 < b_end) load_x(xnext, b + 3);
+    block_mfma(tcur, sh.lut, blk, lane, acc);
+    __syncthreads();  // block b+1's activations are staged and every thread is done with block b's
+  };
+  {
+    load_w(wa, b_begin);
+    if (b_begin + 1 < b_end) load_w(wb, b_begin + 1);
+    XGroup<kXBF16> x0;
+    load_x(x0, b_begin);
+    if (b_begin + 1 < b_end) load_x(xb, b_begin + 1);
+    if (b_begin + 2 < b_end) load_x(xa, b_begin + 2);
+    stage(x0, buf0);
     __syncthreads();
   }
   for (int b = b_begin; b < b_end; b += 2) {
@@ -502,7 +649,12 @@ __device__ int leader_if_first(const KArgs& a, Shared& sh, int z) {
   return sh.flag ? -1 : z;
 }
 
-template <int kMode>
+// kMfma (bf16 activations only): passes of kMfmaMinTokens or more tokens
+// run on the matrix cores.  It is a separate kernel because the extra path
+// changes the compiler's register assignment and loop versioning of the table
+// paths, which then run ~10 % slower; calls expected to have few such passes
+// take the variant without it.
+template <int kMode, bool kMfma>
 __device__ __forceinline__ void gemv_main(const KArgs& a) {
   __shared__ Shared sh;
   const int tid = threadIdx.x;
@@ -511,6 +663,17 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
   const int row = blockIdx.x * kRows + tid;
   const bool row_ok = row < a.n;
 
+  // the matrix-core form's bf16 pattern table (made visible by the barriers
+  // of the unit search below)
+  if (kMfma && threadIdx.x < 32) {
+    const uint32_t c = threadIdx.x;
+    auto bf = [&](int l) -> uint32_t {
+      const int t = code_lane_value(c, l);
+      return t == 0 ? 0u : (t > 0 ? 0x3F80u : 0xBF80u);  // bf16 +1, -1
+    };
+    sh.lut[c] = bf(0) | (bf(1) << 16);
+    sh.lut[32 + c] = bf(2) | (bf(3) << 16);
+  }
   // an invalid pair z gets a row of NaN, whichever workgroup leads below
   {
     const int ez = pair_expert(a, z), tz = pair_token(a, z);
@@ -545,7 +708,9 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
     if (mc == 0) break;
     cursor = __builtin_amdgcn_readfirstlane(sh.next);
     float acc[kMT];
-    switch (mc) {
+    if (kMfma && mc >= kMfmaMinTokens) {
+      run_chunk_mfma(a, sh, wexp, b_begin, b_end, acc);
+    } else switch (mc) {
       case 1: run_chunk<kMode, 1>(a, sh, wexp, b_begin, b_end, acc); break;
       case 2: run_chunk<kMode, 2>(a, sh, wexp, b_begin, b_end, acc); break;
       case 3:  // pair tables take 3 tokens as 4 (the fourth repeats the third, its sums unused)
@@ -572,9 +737,9 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
 // At most 128 VGPRs (4 waves per SIMD, two workgroups per CU as the LDS
 // allows); the fp32-row kernel's pair-table builds need a few bytes of
 // spill outside the block loop to stay there.
-template <int kMode>
+template <int kMode, bool kMfma>
 __global__ __launch_bounds__(kRows, 4) void gemv_kernel(KArgs a) {
-  gemv_main<kMode>(a);
+  gemv_main<kMode, kMfma>(a);
 }
 
 // y[p, r] = sum over the pair's slots s, in order, of partial[s, p, r], for
@@ -650,12 +815,21 @@ int cus_of_current_device() {
 
 // Work of one pass over a block, relative to a one-token pass, for a pass
 // of 1..4 tokens (measured with bf16 activations on a full layer, every
-// expert given the same token count: 1, 1.45, 2.1 and 2.18); an expert with
-// m tokens makes floor(m / 4) four-token passes and one pass of the rest.
-static double block_cost(int m) {
-  constexpr double kPass[5] = {0.0, 1.0, 1.45, 2.1, 2.18};
-  return (m / 4) * kPass[4] + kPass[m % 4];
+// expert given the same token count): on the tables 1, 1.45, 2.1 and 2.18;
+// in the kernel variant with the matrix-core form (3 and 4 tokens there)
+// 1, 1.2, 1.4 and 1.47.  An expert with m tokens makes floor(m / 4)
+// four-token passes and one pass of the rest.
+static double block_cost(int m, bool mfma) {
+  constexpr double kTab[5] = {0.0, 1.0, 1.45, 2.1, 2.18};
+  constexpr double kMat[5] = {0.0, 1.0, 1.2, 1.4, 1.47};
+  const double* c = mfma ? kMat : kTab;
+  return (m / 4) * c[4] + c[m % 4];
 }
+
+// The matrix-core variant pays off once experts commonly hold 3 or more of
+// the call's tokens; it is taken when there are at least as many pairs as
+// experts (bf16 activations only).
+static bool use_mfma(const GemvArgs& a) { return a.x_mode == 1 && a.n_pairs >= a.n_experts; }
 
 // k split: the kernel keeps two workgroups resident per CU (its LDS tables),
 // so workgroups run in rounds of 2 * CUs.  Each split's blocks are parted
@@ -678,6 +852,7 @@ constexpr double kTailShare = 0.2;
 constexpr double kMaxPartialBytes = 1024.0 * 1024.0 * 1024.0;
 
 static void estimate_plan(const GemvArgs& a, int cus, int& best_splits, int& best_bps, int& best_sub) {
+  const bool mfma = use_mfma(a);
   const int nb = static_cast<int>(a.k / kQK);
   const double ntiles = static_cast<double>((a.n + kRows - 1) / kRows);
   const bool parts_ok = a.n_experts <= kLeadExperts;  // beyond, an expert is one unit
@@ -713,7 +888,7 @@ static void estimate_plan(const GemvArgs& a, int cus, int& best_splits, int& bes
       double work = 0.0, longest = 0.0, partial_sums = 0.0;
       for (const auto& [m, count] : cnt) {
         const int parts = std::min(m, max_sub);
-        const double c = block_cost(m) * bps;
+        const double c = block_cost(m, mfma) * bps;
         work += count * (c + kUnitCost * parts);
         if (count >= 0.3) longest = std::max(longest, c / parts + kUnitCost);
         if (splits * parts > 1) partial_sums += m * count * splits * parts;  // pair outputs through scratch
@@ -736,7 +911,7 @@ static void estimate_plan(const GemvArgs& a, int cus, int& best_splits, int& bes
 GemvPlan plan_gemv(const GemvArgs& a, int cus) {
   struct Entry {
     int64_t n_pairs, n_experts, n, k;
-    int cus, splits, bps, sub;
+    int cus, x_mode, splits, bps, sub;
   };
   thread_local Entry cache[16];
   thread_local int cache_used = 0, cache_next = 0;
@@ -746,7 +921,8 @@ GemvPlan plan_gemv(const GemvArgs& a, int cus) {
   int best_splits = 0, best_bps = 0, best_sub = 0;
   for (int i = 0; i < cache_used; ++i) {
     const Entry& c = cache[i];
-    if (c.n_pairs == a.n_pairs && c.n_experts == a.n_experts && c.n == a.n && c.k == a.k && c.cus == cus) {
+    if (c.n_pairs == a.n_pairs && c.n_experts == a.n_experts && c.n == a.n && c.k == a.k && c.cus == cus &&
+        c.x_mode == a.x_mode) {
       best_splits = c.splits;
       best_bps = c.bps;
       best_sub = c.sub;
@@ -755,7 +931,7 @@ GemvPlan plan_gemv(const GemvArgs& a, int cus) {
   }
   if (best_splits == 0) {
     estimate_plan(a, cus, best_splits, best_bps, best_sub);
-    cache[cache_next] = Entry{a.n_pairs, a.n_experts, a.n, a.k, cus, best_splits, best_bps, best_sub};
+    cache[cache_next] = Entry{a.n_pairs, a.n_experts, a.n, a.k, cus, a.x_mode, best_splits, best_bps, best_sub};
     cache_next = (cache_next + 1) % 16;
     cache_used = std::min(cache_used + 1, 16);
   }
@@ -770,6 +946,7 @@ GemvPlan plan_gemv(const GemvArgs& a, int cus) {
       best_sub = parts_ok ? ms : 1;
     }
   }
+  pl.mfma = use_mfma(a);
   pl.blocks_per_split = best_bps;
   pl.splits = best_splits;
   pl.max_sub = best_sub;
@@ -822,8 +999,11 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
   const int ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
   const dim3 grid(ntiles, pl.splits, a.n_pairs);
   switch (ga.x_mode) {
-    case kXBF16: hipLaunchKernelGGL((gemv_kernel<kXBF16>), grid, dim3(kRows), 0, s, a); break;
-    default: hipLaunchKernelGGL((gemv_kernel<kXF32>), grid, dim3(kRows), 0, s, a); break;
+    case kXBF16:
+      if (pl.mfma) hipLaunchKernelGGL((gemv_kernel<kXBF16, true>), grid, dim3(kRows), 0, s, a);
+      else hipLaunchKernelGGL((gemv_kernel<kXBF16, false>), grid, dim3(kRows), 0, s, a);
+      break;
+    default: hipLaunchKernelGGL((gemv_kernel<kXF32, false>), grid, dim3(kRows), 0, s, a); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || pl.partial_bytes == 0 || !reduce) return err;

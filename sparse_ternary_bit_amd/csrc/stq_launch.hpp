@@ -38,6 +38,7 @@ struct GemvPlan {
   int max_sub;         // most parts a split's blocks are cut into for a many-token expert
   int64_t partial_floats;
   int64_t partial_bytes;
+  bool mfma;           // bf16 passes of 3+ tokens on the matrix cores (kernel variant)
 };
 // cus: compute units the plan is made for (see cus_of_stream).
 GemvPlan plan_gemv(const GemvArgs& a, int cus);

@@ -265,14 +265,33 @@ def test_gemv_token_parts_match_oracle(stq, monkeypatch, plan):
                     f"plan {plan} pair {i} (expert {e})")
 
 
-@pytest.mark.parametrize("plan", [None, "2,3"])
-def test_gemv_two_token_tables_match_one_token_tables(stq, monkeypatch, plan):
-    """bf16 activations run passes of 2-4 tokens on two-token tables, fp32
-    activations on one-token tables; the table sums and each token's order of
-    adds are the same, so on bf16-representable activations the two paths
-    must agree bit for bit, for experts with 1-8 tokens."""
-    if plan is not None:
-        monkeypatch.setenv("STQ_GEMV_PLAN", plan)
+def _pass_sizes(pe):
+    """Tokens in the pass that serves each pair: an expert's pairs are taken in
+    pair order, four to a pass."""
+    size = np.zeros(pe.size, dtype=int)
+    for e in np.unique(pe):
+        idx = np.flatnonzero(pe == e)
+        for c in range(0, idx.size, 4):
+            size[idx[c:c + 4]] = min(4, idx.size - c)
+    return size
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+@pytest.mark.parametrize("plan", ["1,1", "3,1"])
+def test_gemv_pair_result_does_not_depend_on_its_companions(stq, monkeypatch, plan, xdt):
+    """Under a plan that does not part experts by token count, a pair's output
+    does not depend on the other pairs batched with it, as long as its pass
+    runs on the same form.  Experts hold 1-8 tokens (passes of 1-4).
+    Passes of 1-2 tokens run on the tables (two-token tables have the sums
+    and per-token order of adds of one-token tables), so such a pair equals
+    the pair computed alone (a one-token pass) bit for bit; fp32 activations
+    always take the tables.  In the bf16 call (as many pairs as experts or
+    more, so the matrix-core kernel variant) passes of 3-4 tokens run on the
+    matrix cores, where a token's results use only its own activations: such
+    a pair equals the same pair in a second call with the pairs in another
+    order (other companions), bit for bit, where it again sits in a pass of
+    3-4 tokens."""
+    monkeypatch.setenv("STQ_GEMV_PLAN", plan)
     rng = np.random.default_rng(63)
     counts = [1, 2, 3, 4, 5, 6, 7, 8]
     n_experts, n, k, n_tokens = len(counts), 320, 2560, 10
@@ -282,12 +301,30 @@ def test_gemv_two_token_tables_match_one_token_tables(stq, monkeypatch, plan):
     pe = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
     pt = np.concatenate([rng.choice(n_tokens, c, replace=False) for c in counts]).astype(np.int32)
     perm = rng.permutation(pe.size)
-    pe, pt = dev(pe[perm]), dev(pt[perm])
+    pe, pt = pe[perm], pt[perm]
     xb, xf = S.bf16_normal(rng, (n_tokens, k))
+    x = dev(xb.view(np.int16)).view(torch.bfloat16) if xdt == "bf16" else dev(xf)
     wt = dev(table)
-    y_bf16 = host(stq.gemv(wt, n * rb, n_experts, n, k, dev(xb.view(np.int16)).view(torch.bfloat16), pe, pt))
-    y_f32 = host(stq.gemv(wt, n * rb, n_experts, n, k, dev(xf), pe, pt))
-    assert np.array_equal(y_bf16.view(np.uint32), y_f32.view(np.uint32))
+    y = host(stq.gemv(wt, n * rb, n_experts, n, k, x, dev(pe), dev(pt)))
+    size = _pass_sizes(pe)
+    matrix = (size >= 3) if xdt == "bf16" else np.zeros(pe.size, bool)
+    for i in np.flatnonzero(~matrix):
+        yi = host(stq.gemv(wt, n * rb, n_experts, n, k, x, dev(pe[i:i + 1]), dev(pt[i:i + 1])))
+        assert np.array_equal(yi[0].view(np.uint32), y[i].view(np.uint32)), (i, int(pe[i]))
+    if matrix.any():
+        order = rng.permutation(pe.size)
+        y2 = host(stq.gemv(wt, n * rb, n_experts, n, k, x, dev(pe[order]), dev(pt[order])))
+        size2 = _pass_sizes(pe[order])
+        checked = 0
+        for j, i in enumerate(order):
+            if matrix[i] and size2[j] >= 3:
+                assert np.array_equal(y2[j].view(np.uint32), y[i].view(np.uint32)), (i, int(pe[i]))
+                checked += 1
+        assert checked >= 8
+    # every pair within the tolerance of the oracle
+    for i in range(pe.size):
+        raw = table[int(pe[i]) * n * rb:(int(pe[i]) + 1) * n * rb]
+        check_close(y[i], O.gemv(raw, n, k, xf[pt[i]]), O.tolerance_scale(raw, n, k, xf[pt[i]])[0], GEMV_TOL, str(i))
 
 
 @pytest.mark.parametrize("per_expert", [2, 3, 4, 9])
