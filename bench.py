@@ -23,8 +23,21 @@ effective bandwidth over the sweep: algorithmic bytes (each touched expert's
 packed bytes once, plus activations and outputs) divided by GEMV time.
 Kernel durations come from HIP events recorded on the launch stream.
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu] [--single-expert] [--copy-calibration]
+After the timed steps, reported beside the headline (not part of `value`):
+  * `single_expert_gemv`: one expert's gate+up GEMV at batch 1 over 100
+    resident experts, 1000 launches (median / p10 / p90), and the same 100
+    calls replayed from a HIP graph;
+  * `roofline_gemm.dense_bf16_gemm_TFLOP/s`: a dense bf16 GEMM of the
+    prefill's total shape through the vendor library (torch.matmul), the
+    matrix-core rate this GPU reaches on a plain contraction;
+  * `stream_read_GB/s`: the library's plain streaming read of 2 GiB;
+  * `cpu_baseline`: the oracle, single-threaded, on bounded samples (GEMV,
+    MoE decode step, encoder, grouped GEMM).
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-single-expert] [--no-dense-ref]
+                  [--no-ffn] [--no-encode] [--no-sensitivity] [--copy-calibration]
   python bench.py --counters FETCH_DIR WRITE_DIR   (summarise rocprofv3 counter runs)
+  python bench.py --source-hashes                  (hashes that stamp the profile summaries)
 
 HBM traffic: two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
 WRITE_SIZE, with --copy-calibration so each run also holds plain copies of a
@@ -152,10 +165,19 @@ def summarise_counters(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
-def cpu_baseline(seconds: float):
-    """The oracle's GEMV, as it stands, on a bounded sample of the decode
-    workload: 512 rows of one expert (the oracle encodes them itself), one
-    token, repeated for about `seconds`."""
+def cpu_baseline():
+    """The oracle as it stands, timed on this host on bounded samples of the
+    workloads (single-threaded: BLAS limited to one thread; the oracle's other
+    array work is single-threaded NumPy):
+      * GEMV: one 4096 x 7168 expert (the oracle's own WLS encoding of expert
+        0's draw), one bf16 token: decode + fp64 dot, in the GPU's
+        algorithmic-byte unit (`value`);
+      * MoE decode step (16 tokens x top-8): 16 of its 128 pairs, each a full
+        expert decode + dot as the oracle does it, scaled to the step;
+      * encoder: WLS (3 rounds) rows/s on the 256 x 1024 case and on 1024
+        rows of the 4096 x 7168 expert;
+      * grouped GEMM: two experts' 64-token slices (decode + fp64 matmul), in
+        useful TFLOP/s."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -163,23 +185,64 @@ def cpu_baseline(seconds: float):
     import synth_inputs as S
     from oracle import stq_oracle as O
 
-    rows = np.arange(512)
-    w = W.expert_weight_rows(W.TABLE_SEED, 0, rows)
-    q = S.calibration_imatrix(W.IMATRIX_SEED, 64, W.K)
-    packed = O.quantize_rows(w, q)
-    xb, xf = S.bf16_normal(np.random.default_rng(4000), (1, W.K))
-    nbytes = packed.nbytes + W.K * 2 + len(rows) * 4
+    env = {k: os.environ[k] for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+           if k in os.environ}
+    host_cores = len(os.sched_getaffinity(0))
+    N, K = W.N_ROWS, W.K
+    q = S.calibration_imatrix(W.IMATRIX_SEED, 64, K)
+    w = W.expert_weight_rows(W.TABLE_SEED, 0, np.arange(N))
+    out = {}
     with threadpool_limits(limits=1):
-        O.gemv(packed, len(rows), W.K, xf[0])                # warm
+        # encoder: the small case, then 1024 rows of the expert; the whole expert is
+        # encoded (untimed past its first 1024 rows) for the GEMV items below
+        w1, q1, _ = S.single_gemv_case()
         t0 = time.perf_counter()
-        calls = 0
-        while time.perf_counter() - t0 < seconds:
-            O.gemv(packed, len(rows), W.K, xf[0])
-            calls += 1
-        dt = time.perf_counter() - t0
-    return {"value": round(nbytes * calls / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle GEMV (decode + fp64 dot) of 512 rows x 7168 of one expert, one bf16 token, "
-                      f"{calls} calls in {dt:.1f} s; same algorithmic-byte count as the GPU figure"}
+        O.quantize_rows(w1, q1)
+        t_small = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        parts = [O.quantize_rows(w[:1024], q)]
+        t_big = time.perf_counter() - t0
+        for r in range(1024, N, 1024):
+            parts.append(O.quantize_rows(w[r:r + 1024], q))
+        # row tiles of 64 rows are whole inside each 1024-row part, so the parts concatenate
+        packed = np.concatenate([p.reshape(-1) for p in parts])
+        del w
+        xb, xf = S.bf16_normal(np.random.default_rng(4000), (16, K))
+        expert_bytes = packed.nbytes
+        # GEMV, one expert, one token
+        O.gemv(packed, N, K, xf[0])                           # warm
+        t0 = time.perf_counter()
+        reps = 3
+        for i in range(reps):
+            O.gemv(packed, N, K, xf[i])
+        t_gemv = (time.perf_counter() - t0) / reps
+        gemv_gbs = (expert_bytes + K * 2 + N * 4) / t_gemv / 1e9
+        # MoE decode step sample: 16 pairs (each decodes its expert), scaled to 128 pairs
+        t0 = time.perf_counter()
+        for i in range(16):
+            O.gemv(packed, N, K, xf[i])
+        t16 = time.perf_counter() - t0
+        step_bytes = 101.96 * expert_bytes + 16 * K * 2 + 128 * N * 4
+        step_s = t16 * 128 / 16
+        # grouped GEMM sample: two experts x 64 tokens
+        table = np.concatenate([packed, packed])
+        xg = xf[np.arange(128) % 16]
+        offs = np.array([0, 64, 128], dtype=np.int32)
+        t0 = time.perf_counter()
+        O.grouped_gemm(table, expert_bytes, N, K, xg, offs)
+        t_gemm = time.perf_counter() - t0
+    out = {"value": round(gemv_gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": (f"oracle GEMV of one 4096x7168 expert (decode + fp64 dot), one bf16 token, "
+                      f"{reps} calls of {t_gemv:.2f} s; same algorithmic-byte count as the GPU figure. "
+                      f"Single-threaded (BLAS limited to 1 thread); host has {host_cores} cores"),
+           "host_cores": host_cores, "blas_threads": 1, "thread_env": env,
+           "moe_decode_step_16x8": {"s_per_step": round(step_s, 2), "GB/s": round(step_bytes / step_s / 1e9, 4),
+                                    "sample": "16 of the 128 pairs, scaled"},
+           "encode_rows_per_s": {"256x1024": round(256 / t_small, 1), "4096x7168_expert": round(1024 / t_big, 1),
+                                 "sample": "WLS, 3 rounds; 1024 rows of the expert"},
+           "grouped_gemm": {"TFLOP/s": round(2.0 * 128 * N * K / t_gemm / 1e12, 6), "s": round(t_gemm, 2),
+                            "sample": "2 experts x 64 tokens of the 2048-token prefill shape"}}
+    return out
 
 
 def main() -> int:
@@ -188,9 +251,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--single-expert", action="store_true",
-                    help="also time the batch-1 single-expert GEMV over 100 resident experts")
+    ap.add_argument("--no-single-expert", action="store_true",
+                    help="skip the single-expert GEMV over 100 resident experts (1000 launches)")
+    ap.add_argument("--no-dense-ref", action="store_true",
+                    help="skip the dense bf16 GEMM reference (hipBLASLt through torch) beside the grouped GEMM")
     ap.add_argument("--no-encode", action="store_true",
                     help="skip the timed layer-scale encode (8 experts, both encoders)")
     ap.add_argument("--no-sensitivity", action="store_true",
@@ -201,9 +265,15 @@ def main() -> int:
                     help=f"after timing, copy {COPY_MIB} MiB device to device {COPY_REPS} times (counter calibration)")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/hbm_counters.json")
+    ap.add_argument("--source-hashes", action="store_true",
+                    help="print the kernel-source hashes that stamp the profile summaries")
     args = ap.parse_args()
     if args.counters:
         return summarise_counters(*args.counters)
+    if args.source_hashes:
+        for name in ("k_gemv.hip", "k_gemm.hip", "k_moe.hip", "k_codec.hip", "k_sens.hip", "k_probe.hip"):
+            print(f"{name} {kernel_source_hash(name)}")
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the STQ1_0 path here has no multi-GPU mode "
@@ -263,10 +333,11 @@ def main() -> int:
     y_pre = torch.empty((total_m, N), dtype=torch.float32, device=dev)
     gemm_flop = 2.0 * total_m * N * K
 
-    if args.single_expert:
-        xs1 = [S.torch_bf16_normal(4000 + i, (1, K), device=dev) for i in range(100)]
-        pes1 = [torch.tensor([i], dtype=torch.int32, device=dev) for i in range(100)]
-        ys1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+    # workspaces for the timed calls, sized once (the library allocates nothing)
+    ws_gemv = torch.empty(max(stq.gemv_plan(E, N, K, B * W.TOP_K)[2] for B in BATCHES + (1,)) + 256,
+                          dtype=torch.uint8, device=dev)
+    ws_ffn = torch.empty(max(stq.moe_ffn_workspace(E, K, W.D_FF, B, W.TOP_K) for B in FFN_BATCHES) + 256,
+                         dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -275,6 +346,14 @@ def main() -> int:
         return torch.cuda.Event(enable_timing=True)
 
     def run_step(s, rec):
+        # the prefill GEMM first: while it runs, the host queues the decode
+        # sweep behind it, so the short GEMV calls run back to back instead of
+        # waiting on the host between calls
+        a, b = ev(), ev()
+        a.record(stream)
+        stq.grouped_gemm(t_wls, stride, E, N, K, x_sorted, offsets_t, out=y_pre)
+        b.record(stream)
+        rec["gemm"].append((a, b))
         # the two encodings of each batch back to back, first one then the
         # other on alternate steps, so both see the same neighbouring work
         # (the amax copy checks that speed does not depend on the encoder)
@@ -283,33 +362,22 @@ def main() -> int:
             for enc in order:
                 a, b = ev(), ev()
                 a.record(stream)
-                stq.gemv(tables[enc], stride, E, N, K, x, pe_t, pt_t, out=y)
+                stq.gemv(tables[enc], stride, E, N, K, x, pe_t, pt_t, out=y, workspace=ws_gemv)
                 b.record(stream)
                 rec["gemv"].append((enc, B, nbytes, uniq, a, b))
-        a, b = ev(), ev()
-        a.record(stream)
-        stq.grouped_gemm(t_wls, stride, E, N, K, x_sorted, offsets_t, out=y_pre)
-        b.record(stream)
-        rec["gemm"].append((a, b))
         for (B, pe_t, pw, x, y, nbytes) in ([] if args.no_ffn else sweep[s][1]):
             a, b = ev(), ev()
             a.record(stream)
-            stq.moe_ffn_decode(t_wls, stride, t_down, down_stride, E, K, W.D_FF, x, pe_t, pw, W.TOP_K, out=y)
+            stq.moe_ffn_decode(t_wls, stride, t_down, down_stride, E, K, W.D_FF, x, pe_t, pw, W.TOP_K, out=y,
+                               workspace=ws_ffn)
             b.record(stream)
             rec["ffn"].append((B, nbytes, a, b))
-        if args.single_expert:
-            for i in range(100):
-                a, b = ev(), ev()
-                a.record(stream)
-                stq.gemv(t_wls, stride, E, N, K, xs1[i], pes1[i], out=ys1)
-                b.record(stream)
-                rec["single"].append((a, b))
 
     for s in range(args.warmup):
-        run_step(s, {"gemv": [], "gemm": [], "single": [], "ffn": []})
+        run_step(s, {"gemv": [], "gemm": [], "ffn": []})
     torch.cuda.synchronize()
 
-    rec = {"gemv": [], "gemm": [], "single": [], "ffn": []}
+    rec = {"gemv": [], "gemm": [], "ffn": []}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.warmup, total_steps):
@@ -410,6 +478,81 @@ def main() -> int:
                     "full_over_diag": round(float(ef.sum() / ed.sum()), 4)}
         del w0, xc, w0_hat, ef, ed, q2o
 
+    single_out = None
+    if not args.no_single_expert:
+        # one expert's gate+up GEMV at batch 1 over 100 resident experts
+        # (481.7 MB, beyond the 256 MB last-level cache), one launch per expert in
+        # rotation, 1000 launches in all; a short spin on the GPU before each
+        # rotation lets the host queue the rotation ahead of the GPU, so each
+        # launch's events bracket the kernels alone
+        xs1 = [S.torch_bf16_normal(4000 + i, (1, K), device=dev) for i in range(100)]
+        pes1 = [torch.tensor([i], dtype=torch.int32, device=dev) for i in range(100)]
+        ys1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+        ws1 = torch.empty(max(1, stq.gemv_plan(E, N, K, 1)[2]), dtype=torch.uint8, device=dev)
+        for i in range(100):
+            stq.gemv(t_wls, stride, E, N, K, xs1[i], pes1[i], out=ys1, workspace=ws1)
+        torch.cuda.synchronize()
+        evs = []
+        for rot in range(10):
+            torch.cuda._sleep(20_000_000)
+            for i in range(100):
+                a, b = ev(), ev()
+                a.record(stream)
+                stq.gemv(t_wls, stride, E, N, K, xs1[i], pes1[i], out=ys1, workspace=ws1)
+                b.record(stream)
+                evs.append((a, b))
+            torch.cuda.synchronize()
+        sm = [a.elapsed_time(b) for (a, b) in evs]
+        sb = expert_bytes + K * 2 + N * 4
+        single_out = {"launches": len(sm), "experts_resident": 100, "bytes_per_call": sb,
+                      "us_median": round(1e3 * float(np.median(sm)), 2),
+                      "us_p10": round(1e3 * float(np.percentile(sm, 10)), 2),
+                      "us_p90": round(1e3 * float(np.percentile(sm, 90)), 2),
+                      "GB/s_median": round(sb / (float(np.median(sm)) * 1e-3) / 1e9, 1)}
+        # the same 100 calls captured once into a HIP graph and replayed: a
+        # decode loop's per-call cost without host launch gaps
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(100):
+                    stq.gemv(t_wls, stride, E, N, K, xs1[i], pes1[i], out=ys1, workspace=ws1)
+        torch.cuda.current_stream().wait_stream(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(5):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per = a.elapsed_time(b) / 500
+        single_out["graph_us_per_call"] = round(1e3 * per, 2)
+        single_out["graph_GB/s"] = round(sb / (per * 1e-3) / 1e9, 1)
+        del g, xs1, pes1, ys1, ws1
+
+    dense_out = None
+    if not args.no_dense_ref:
+        # the MFMA rate a dense bf16 GEMM of the prefill's total shape reaches on
+        # this GPU through the vendor library (hipBLASLt via torch.matmul):
+        # [16384 x 7168] x [7168 x 4096], fp32 accumulation, bf16 out
+        xa = torch.randn((total_m, K), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        wb = torch.randn((K, N), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        for _ in range(3):
+            yd = xa @ wb
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(10):
+            yd = xa @ wb
+        b.record(stream)
+        torch.cuda.synchronize()
+        dms = a.elapsed_time(b) / 10
+        dense_out = {"dense_bf16_gemm_TFLOP/s": round(gemm_flop / (dms * 1e-3) / 1e12, 1),
+                     "dense_bf16_gemm_us": round(1e3 * dms, 1)}
+        del xa, wb, yd
+
     # ---------------- results ----------------
     gemv_ms = [a.elapsed_time(b) for (_, _, _, _, a, b) in rec["gemv"]]
     gemv_bytes = [nb for (_, _, nb, _, _, _) in rec["gemv"]]
@@ -478,36 +621,13 @@ def main() -> int:
     if ffn:
         out["moe_ffn_decode"] = {"layer": "256 experts, top-8, gate/up 4096x7168 + down 7168x2048, STQ1_0",
                                  "bytes": "touched experts' packed gate/up and down matrices, x and y", **ffn}
-    if rec["single"]:
-        sm = [a.elapsed_time(b) for (a, b) in rec["single"]]
-        sb = expert_bytes + K * 2 + N * 4
-        out["single_expert_gemv"] = {"us_median": round(1e3 * float(np.median(sm)), 2),
-                                     "us_p10": round(1e3 * float(np.percentile(sm, 10)), 2),
-                                     "us_p90": round(1e3 * float(np.percentile(sm, 90)), 2),
-                                     "GB/s_median": round(sb / (float(np.median(sm)) * 1e-3) / 1e9, 1)}
-        # the same 100 calls captured once into a HIP graph and replayed: a
-        # decode loop's per-call cost without host launch gaps
-        g = torch.cuda.CUDAGraph()
-        cs = torch.cuda.Stream()
-        cs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cs):
-            with torch.cuda.graph(g, stream=cs):
-                for i in range(100):
-                    stq.gemv(t_wls, stride, E, N, K, xs1[i], pes1[i], out=ys1)
-        torch.cuda.current_stream().wait_stream(cs)
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = ev(), ev()
-        a.record(stream)
-        for _ in range(5):
-            g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        per = a.elapsed_time(b) / 500
-        out["single_expert_gemv"]["graph_us_per_call"] = round(1e3 * per, 2)
-        out["single_expert_gemv"]["graph_GB/s"] = round(sb / (per * 1e-3) / 1e9, 1)
+    if single_out:
+        out["single_expert_gemv"] = single_out
+    if dense_out:
+        out["roofline_gemm"].update(dense_out)
+        out["roofline_gemm"]["frac_of_dense_bf16_gemm"] = round(gemm_tflops / dense_out["dense_bf16_gemm_TFLOP/s"], 4)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
     return 0
 

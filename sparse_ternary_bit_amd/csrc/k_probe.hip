@@ -1,7 +1,8 @@
 // Streaming-read reference for the HBM roofline: reads a device buffer once
-// with 16-byte loads (four in flight per thread, grid-stride) and folds the
-// words into one value, so the rate it reaches is what this GPU sustains for
-// plain reads, measured beside the decode GEMV's effective bandwidth.
+// with 16-byte loads (four in flight per thread, grid-stride) and folds every
+// word of every load into one value (so no load can be narrowed), so the rate
+// it reaches is what this GPU sustains for plain reads, measured beside the
+// decode GEMV's effective bandwidth.
 #include "stq_launch.hpp"
 
 namespace stq {
@@ -16,11 +17,12 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
   uint32_t s = 0;
   int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  auto fold = [](u32x4_t v) { return (v.x ^ v.y) + (v.z ^ v.w); };
   for (; i + 3 * stride < n; i += 4 * stride) {
     const u32x4_t a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    s += (a.x ^ b.y) ^ (c.z ^ d.w);
+    s += (fold(a) ^ fold(b)) + (fold(c) ^ fold(d));
   }
-  for (; i < n; i += stride) s += p[i].x;
+  for (; i < n; i += stride) s += fold(p[i]);
   // the fold is kept only if it can reach memory; the one-word sink is
   // written by at most the threads whose fold matches a fixed tag
   if (s == 0x5EED5EEDu) sink[0] = s;
