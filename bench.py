@@ -38,6 +38,9 @@ After the timed steps, reported beside the headline (not part of `value`):
                   [--no-ffn] [--no-encode] [--no-sensitivity] [--copy-calibration]
   python bench.py --counters FETCH_DIR WRITE_DIR   (summarise rocprofv3 counter runs)
   python bench.py --source-hashes                  (hashes that stamp the profile summaries)
+  python bench.py --trace-summary TRACE_DIR --steps K --warmup W
+                                                   (per-kernel times of the timed steps from a
+                                                    rocprofv3 --kernel-trace run of the same K, W)
 
 HBM traffic: two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
 WRITE_SIZE, with --copy-calibration so each run also holds plain copies of a
@@ -165,6 +168,41 @@ def summarise_counters(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
+def summarise_trace(trace_dir: str, warmup: int, steps: int) -> int:
+    """Per-kernel durations from a rocprofv3 --kernel-trace run of this script:
+    for every kernel called a multiple of (warmup + steps) times, the mean,
+    min and max over the dispatches of the timed steps (the first warmup
+    shares, by start time, are left out), beside the mean over all calls."""
+    import csv
+    import glob
+    rows = {}
+    for f in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "")
+                rows.setdefault(name, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    if not rows:
+        print(f"no kernel_trace.csv under {trace_dir}", file=sys.stderr)
+        return 1
+    total = warmup + steps
+    print("| Kernel | Calls | Timed calls | Mean timed us | Min us | Max us | Mean all us |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    out = []
+    for name, ds in rows.items():
+        ds.sort()
+        dur = [(e - b) / 1e3 for b, e in ds]
+        timed = dur[warmup * len(dur) // total:] if len(dur) % total == 0 else []
+        out.append((sum(dur), name, len(dur), timed, dur))
+    for _, name, n, timed, dur in sorted(out, reverse=True):
+        short = name if len(name) <= 70 else name[:70] + "..."
+        if timed:
+            print(f"| {short} | {n} | {len(timed)} | {sum(timed) / len(timed):.1f} | {min(timed):.1f} | "
+                  f"{max(timed):.1f} | {sum(dur) / n:.1f} |")
+        else:
+            print(f"| {short} | {n} | - | - | {min(dur):.1f} | {max(dur):.1f} | {sum(dur) / n:.1f} |")
+    return 0
+
+
 def cpu_baseline():
     """The oracle as it stands, timed on this host on bounded samples of the
     workloads (single-threaded: BLAS limited to one thread; the oracle's other
@@ -267,9 +305,13 @@ def main() -> int:
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/hbm_counters.json")
     ap.add_argument("--source-hashes", action="store_true",
                     help="print the kernel-source hashes that stamp the profile summaries")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 --kernel-trace run of this script made with the same --steps/--warmup")
     args = ap.parse_args()
     if args.counters:
         return summarise_counters(*args.counters)
+    if args.trace_summary:
+        return summarise_trace(args.trace_summary, args.warmup, args.steps)
     if args.source_hashes:
         for name in ("k_gemv.hip", "k_gemm.hip", "k_moe.hip", "k_codec.hip", "k_sens.hip", "k_probe.hip"):
             print(f"{name} {kernel_source_hash(name)}")

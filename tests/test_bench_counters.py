@@ -83,3 +83,34 @@ def test_traffic_is_reported_only_for_the_counted_source(tmp_path, monkeypatch):
     out.write_text(json.dumps({"k_gemv.hip": {"source_hash": "0" * 16, "bytes_per_launch": 123}}))
     assert bench.measured_traffic("k_gemv.hip") is None  # the kernel changed since
 
+
+
+def test_trace_summary_drops_warmup_dispatches(tmp_path, capsys):
+    """Kernels called once or eight times per step: the timed mean leaves out
+    the warm-up steps' dispatches (the first ones by start time, whatever the
+    row order); a kernel called at no multiple of the step count (setup) has
+    no timed figure."""
+    d = tmp_path / "trace"
+    d.mkdir()
+    rows, t = [], 0
+    for step in range(7):                                  # 2 warm-up + 5 timed steps
+        for _ in range(8):
+            rows.append(("void stq::gemv_kernel<1, false>(KArgs)", t, t + 100_000 + 1000 * step))
+            t += 200_000
+        rows.append(("stq::grouped_gemm_kernel(GArgs)", t, t + (2_000_000 if step < 2 else 1_000_000)))
+        t += 3_000_000
+    rows.append(("setup_kernel", 5, 10))
+    rows.reverse()
+    with open(d / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, b, e in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": b, "End_Timestamp": e})
+    assert bench.summarise_trace(str(d), warmup=2, steps=5) == 0
+    out = capsys.readouterr().out
+    gemm = next(l for l in out.splitlines() if "grouped_gemm" in l).split("|")
+    assert [c.strip() for c in gemm[2:8]] == ["7", "5", "1000.0", "1000.0", "1000.0", "1285.7"]
+    gemv = next(l for l in out.splitlines() if "gemv_kernel" in l).split("|")
+    assert [c.strip() for c in gemv[2:5]] == ["56", "40", "104.0"]   # steps 2..6: 102..106 us
+    setup = next(l for l in out.splitlines() if "setup_kernel" in l).split("|")
+    assert setup[3].strip() == "-"
