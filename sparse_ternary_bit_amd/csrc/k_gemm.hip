@@ -101,10 +101,19 @@ __device__ __forceinline__ float opaque_zero() {
 }
 
 // A pass: tokens [row0, row0 + mt) of the sorted activations, NT = ceil(mt/16).
+// The thread index through an opaque move: values derived from it are then
+// computed in each pass instead of being hoisted to the kernel's start, where
+// the register pressure of the passes would spill them to scratch memory.
+__device__ __forceinline__ int pass_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(static_cast<int>(threadIdx.x)));
+  return t;
+}
+
 template <int NT>
 __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t* wexp, int slab, int64_t row0,
                                          int mt) {
-  const int tid = threadIdx.x;
+  const int tid = pass_tid();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, r = lane & 15;
