@@ -346,16 +346,21 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   const int rowbase = blockIdx.x * kRows + wave * 64;
   const int valid = max(0, min(kTileRows, a.n - rowbase));
   const uint8_t* tb = wexp + static_cast<int64_t>(min(rowbase, a.n)) * a.nb * kBlockBytes;
-  const Rsrc rs = make_rsrc(tb, (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u);
+  const uint32_t tile_bytes = (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u;
+  const Rsrc rs = make_rsrc(tb, tile_bytes);
+  // a block past b_end is "loaded" from the end of the tile's range, where the
+  // range check returns zeros without a memory access: the load stays
+  // unconditional (a skipped load makes the compiler copy the previous block
+  // into the load's registers first)
   auto load_w = [&](RawBlock& r, int b) {
-    load_raw_block(rs, (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes, r);
+    const uint32_t off = b < b_end ? (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes : tile_bytes;
+    load_raw_block(rs, off, r);
   };
+  // every thread loads (threads without a table item load token 0's group)
   auto load_x = [&](XGroup<kMode> (&x)[2], int b) {
     const int64_t col = static_cast<int64_t>(b) * kQK + 4 * it_g;
-    if (has0) {
-      x[0].load(a, tok0, col);
-      if (kPair) x[1].load(a, tok1, col);
-    }
+    x[0].load(a, tok0, col);
+    if (kPair) x[1].load(a, tok1, col);
   };
   auto build = [&](const XGroup<kMode> (&x)[2], char* t) {
     if constexpr (kPair) {
@@ -369,34 +374,36 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
   char* buf0 = sh.tab[0];
   char* buf1 = sh.tab[1];
 
-  // Pipeline over blocks j = b - b_begin: weights of blocks j, j+1 and
-  // activations of blocks j+1, j+2 are in flight; block j uses weight slot
-  // j&1, table buffer j&1, and builds table j+1 from activation slot (j+1)&1.
-  RawBlock wa, wb;
-  XGroup<kMode> xa[2], xb[2];
-  auto step = [&](RawBlock& wcur, XGroup<kMode> (&xnext)[2], char* tcur, char* tnext, int b) {
+  // Pipeline over blocks: while block b is multiplied, the weights of block
+  // b+1 and the activations of block b+2 are in flight, and table b+1 is
+  // built from activations loaded one block earlier.  Each stream has one
+  // register set: a load reuses the registers its predecessor was read from,
+  // so no copy of an in-flight load (which would wait for it) is needed.
+  RawBlock w;
+  XGroup<kMode> xn[2];
+  auto step = [&](char* tcur, char* tnext, int b) {
     const bool odd = ((static_cast<uint32_t>(b) * valid) & 1u) ? !lane_odd : lane_odd;
-    const Block blk = realign_block(wcur, odd);
-    if (b + 1 < b_end) build(xnext, tnext);
-    if (b + 2 < b_end) load_w(wcur, b + 2);
-    if (b + 3 < b_end) load_x(xnext, b + 3);
+    const Block blk = realign_block(w, odd);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(w, b + 1);
+    if (b + 1 < b_end) build(xn, tnext);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(xn, min(b + 2, b_end - 1));
     if constexpr (kPair) block_dot_pairs<MC>(tcur, blk, acc);
     else block_dot<MC>(tcur, blk, acc);
     __syncthreads();  // table b+1 is complete and every thread is done with table b
   };
   {
-    load_w(wa, b_begin);
-    if (b_begin + 1 < b_end) load_w(wb, b_begin + 1);
+    load_w(w, b_begin);
     XGroup<kMode> x0[2];
     load_x(x0, b_begin);
-    if (b_begin + 1 < b_end) load_x(xb, b_begin + 1);
-    if (b_begin + 2 < b_end) load_x(xa, b_begin + 2);
+    load_x(xn, min(b_begin + 1, b_end - 1));
     build(x0, buf0);
     __syncthreads();
   }
   for (int b = b_begin; b < b_end; b += 2) {
-    step(wa, xb, buf0, buf1, b);
-    if (b + 1 < b_end) step(wb, xa, buf1, buf0, b + 1);
+    step(buf0, buf1, b);
+    if (b + 1 < b_end) step(buf1, buf0, b + 1);
   }
 }
 
@@ -478,7 +485,7 @@ __device__ __forceinline__ void block_mfma(const char* xs, const uint32_t* lut, 
 // Blocks [b_begin, b_end) of this workgroup's rows for bf16 activations and
 // up to four tokens on the matrix cores (token slots past the pass's count
 // repeat its last token; their results are not stored).  The pipeline is
-// run_chunk's: weights two blocks ahead, activations three; each block's
+// run_chunk's: weights one block ahead, activations two; each block's
 // activations (4 tokens x 64 groups x 8 bytes) are staged in LDS in
 // [group][token] order while the previous block is multiplied.
 __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const uint8_t* wexp, int b_begin,
@@ -502,13 +509,18 @@ __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const
   const int rowbase = blockIdx.x * kRows + wave * 64;
   const int valid = max(0, min(kTileRows, a.n - rowbase));
   const uint8_t* tb = wexp + static_cast<int64_t>(min(rowbase, a.n)) * a.nb * kBlockBytes;
-  const Rsrc rs = make_rsrc(tb, (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u);
+  const uint32_t tile_bytes = (static_cast<uint32_t>(valid) * a.nb * kBlockBytes + 3u) & ~3u;
+  const Rsrc rs = make_rsrc(tb, tile_bytes);
+  // a block past b_end is "loaded" from the end of the tile's range, where the
+  // range check returns zeros without a memory access: the load stays
+  // unconditional (a skipped load makes the compiler copy the previous block
+  // into the load's registers first)
   auto load_w = [&](RawBlock& r, int b) {
-    load_raw_block(rs, (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes, r);
+    const uint32_t off = b < b_end ? (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes : tile_bytes;
+    load_raw_block(rs, off, r);
   };
-  auto load_x = [&](XGroup<kXBF16>& x, int b) {
-    if (stages) x.load(a, tok_st, static_cast<int64_t>(b) * kQK + 4 * st_g);
-  };
+  // every thread loads (threads 256.. load token 0's group and stage nothing)
+  auto load_x = [&](XGroup<kXBF16>& x, int b) { x.load(a, tok_st, static_cast<int64_t>(b) * kQK + 4 * st_g); };
   auto stage = [&](const XGroup<kXBF16>& x, char* t) {
     if (stages) *reinterpret_cast<uint2*>(t + st_off) = make_uint2(x.v[0], x.v[1]);
   };
@@ -516,30 +528,31 @@ __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const
   char* buf0 = sh.tab[0];
   char* buf1 = sh.tab[1];
 
-  RawBlock wa, wb;
-  XGroup<kXBF16> xa, xb;
-  auto step = [&](RawBlock& wcur, XGroup<kXBF16>& xnext, char* tcur, char* tnext, int b) {
+  // one register set per stream, as in run_chunk
+  RawBlock w;
+  XGroup<kXBF16> xn;
+  auto step = [&](char* tcur, char* tnext, int b) {
     const bool odd = ((static_cast<uint32_t>(b) * valid) & 1u) ? !lane_odd : lane_odd;
-    const Block blk = realign_block(wcur, odd);
-    if (b + 1 < b_end) stage(xnext, tnext);
-    if (b + 2 < b_end) load_w(wcur, b + 2);
-    if (b + 3 < b_end) load_x(xnext, b + 3);
+    const Block blk = realign_block(w, odd);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(w, b + 1);
+    if (b + 1 < b_end) stage(xn, tnext);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(xn, min(b + 2, b_end - 1));
     block_mfma(tcur, sh.lut, blk, lane, acc);
     __syncthreads();  // block b+1's activations are staged and every thread is done with block b's
   };
   {
-    load_w(wa, b_begin);
-    if (b_begin + 1 < b_end) load_w(wb, b_begin + 1);
+    load_w(w, b_begin);
     XGroup<kXBF16> x0;
     load_x(x0, b_begin);
-    if (b_begin + 1 < b_end) load_x(xb, b_begin + 1);
-    if (b_begin + 2 < b_end) load_x(xa, b_begin + 2);
+    load_x(xn, min(b_begin + 1, b_end - 1));
     stage(x0, buf0);
     __syncthreads();
   }
   for (int b = b_begin; b < b_end; b += 2) {
-    step(wa, xb, buf0, buf1, b);
-    if (b + 1 < b_end) step(wb, xa, buf1, buf0, b + 1);
+    step(buf0, buf1, b);
+    if (b + 1 < b_end) step(buf1, buf0, b + 1);
   }
 }
 
