@@ -429,18 +429,16 @@ __device__ __forceinline__ f32x4_t mfma_group(const s16x4_t (&xa)[4], s16x4_t w,
   return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(xa[G >> 4], w, c, 4, G & 15, 0);
 }
 
-// Code word W (groups 8W..8W+7) of one block: pattern reads, then the MFMAs
-// of the four low-nibble groups into c0 and the four high-nibble ones into c1.
+// Code word W (groups 8W..8W+7) of one block: the pattern reads, bl for the
+// four low-nibble groups and bu for the four high-nibble ones.
 template <int W>
-__device__ __forceinline__ void word_mfma(const Block& blk, const char* lb, const s16x4_t (&xa)[4], f32x4_t& c0,
-                                          f32x4_t& c1) {
+__device__ __forceinline__ void word_patterns(const Block& blk, const char* lb, s16x4_t (&bl)[4], s16x4_t (&bu)[4]) {
   const uint32_t Q = blk.qs[W];
   const uint32_t Hs = blk.qh[W >> 2] << (6 - 2 * (W & 3));
   // byte j of cl / cu = 4 * code of group 8W+j / 8W+4+j
   uint32_t cl = ((Q << 2) & 0x3C3C3C3Cu) | (Hs & 0x40404040u);
   uint32_t cu = ((Q >> 2) & 0x3C3C3C3Cu) | ((Hs >> 1) & 0x40404040u);
   asm("" : "+v"(cl), "+v"(cu));  // one bit-field extract per code, as in block_dot
-  s16x4_t bl[4], bu[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t ol = __builtin_amdgcn_ubfe(cl, 8 * j, 8);
@@ -452,6 +450,12 @@ __device__ __forceinline__ void word_mfma(const Block& blk, const char* lb, cons
     bl[j] = __builtin_bit_cast(s16x4_t, (l1 << 32) | l0);
     bu[j] = __builtin_bit_cast(s16x4_t, (u1 << 32) | u0);
   }
+}
+
+// The MFMAs of code word W: its low-nibble groups into c0, high into c1.
+template <int W>
+__device__ __forceinline__ void word_mfmas(const s16x4_t (&xa)[4], const s16x4_t (&bl)[4], const s16x4_t (&bu)[4],
+                                           f32x4_t& c0, f32x4_t& c1) {
   c0 = mfma_group<8 * W + 0>(xa, bl[0], c0);
   c1 = mfma_group<8 * W + 4>(xa, bu[0], c1);
   c0 = mfma_group<8 * W + 1>(xa, bl[1], c0);
@@ -462,6 +466,22 @@ __device__ __forceinline__ void word_mfma(const Block& blk, const char* lb, cons
   c1 = mfma_group<8 * W + 7>(xa, bu[3], c1);
 }
 
+// Words W and up: the pattern reads of word W+1 are issued before the MFMAs
+// of word W, so the reads of one word are in flight while the previous
+// word's products run.
+template <int W>
+__device__ __forceinline__ void words_from(const Block& blk, const char* lb, const s16x4_t (&xa)[4],
+                                           s16x4_t (&bl)[4], s16x4_t (&bu)[4], f32x4_t& c0, f32x4_t& c1) {
+  if constexpr (W < 7) {
+    s16x4_t nl[4], nu[4];
+    word_patterns<W + 1>(blk, lb, nl, nu);
+    word_mfmas<W>(xa, bl, bu, c0, c1);
+    words_from<W + 1>(blk, lb, xa, nl, nu, c0, c1);
+  } else {
+    word_mfmas<W>(xa, bl, bu, c0, c1);
+  }
+}
+
 __device__ __forceinline__ void block_mfma(const char* xs, const uint32_t* lut, const Block& blk, int lane,
                                            float (&acc)[kMT]) {
   const float d = half_bits_to_float(blk.d16);
@@ -470,14 +490,9 @@ __device__ __forceinline__ void block_mfma(const char* xs, const uint32_t* lut, 
   for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const s16x4_t*>(xs + (64 * s + lane) * 8);
   f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = {0.0f, 0.0f, 0.0f, 0.0f};
   const char* lb = reinterpret_cast<const char*>(lut);
-  word_mfma<0>(blk, lb, xa, c0, c1);
-  word_mfma<1>(blk, lb, xa, c0, c1);
-  word_mfma<2>(blk, lb, xa, c0, c1);
-  word_mfma<3>(blk, lb, xa, c0, c1);
-  word_mfma<4>(blk, lb, xa, c0, c1);
-  word_mfma<5>(blk, lb, xa, c0, c1);
-  word_mfma<6>(blk, lb, xa, c0, c1);
-  word_mfma<7>(blk, lb, xa, c0, c1);
+  s16x4_t bl[4], bu[4];
+  word_patterns<0>(blk, lb, bl, bu);
+  words_from<0>(blk, lb, xa, bl, bu, c0, c1);
 #pragma unroll
   for (int m = 0; m < kMT; ++m) acc[m] = fmaf(d, c0[m] + c1[m], acc[m]);
 }
