@@ -18,7 +18,10 @@
 // code (already scaled by 4) and, per token, one LDS read with the group's
 // table offset as an immediate plus one fp32 add; the block's fp16 scale
 // multiplies the block sum.  All threads of a wavefront read the same group's
-// 128-byte table at once, so the reads are bank-conflict free.  With 2-4
+// 128-byte table at once, so the reads are bank-conflict free.  Group tables
+// sit 16 bytes more than their size apart, so that the 16-byte stores that
+// build them (a wavefront writes 16 neighbouring groups' tables at once) fall
+// on all eight 16-byte bank groups instead of two or four.  With 2-4
 // tokens in a pass, two tokens share an 8-byte table entry and one 8-byte
 // read serves both (an LDS read issues at the same rate for 4 and 8 bytes,
 // and the table reads bound the extra tokens of a pass).
@@ -30,7 +33,7 @@
 // thread loads the 11 aligned words that cover its own 42-byte block with
 // 16 + 16 + 12-byte buffer loads (the wavefront's loads cover the run with no
 // gaps and never leave it) and realigns them with byte permutes.  Loads run
-// two blocks ahead, in the order they are consumed.
+// one block ahead, in the order they are consumed.
 //
 // k split: the blocks of a row may be split over several workgroups (chosen
 // per call from the expected number of active experts, see plan_gemv), and
@@ -57,16 +60,19 @@ namespace {
 constexpr int kRows = 512;                 // rows (= threads) per workgroup
 constexpr int kWaves = kRows / 64;
 constexpr int kMT = 4;                     // tokens per pass
-constexpr int kTabBytes = kGroups * 32 * 4;
-constexpr int kTokStride = kTabBytes + 16; // token tables apart by a non-multiple of 256 bytes
-constexpr int kBufBytes = kMT * kTokStride;
-// Passes of 2 or more tokens tabulate two tokens to an 8-byte entry: group g's 256-byte table at g * 256, the second pair's
-// tables kPairStride further (16-byte aligned and not a multiple of 512, so
-// the compiler keeps the two pairs' reads apart instead of fusing them into
-// one 16-byte read that it then waits on read by read).
-constexpr int kPairTab = kGroups * 32 * 8;
+// One-token passes: group g's 128-byte table at g * kGrp1.
+constexpr int kGrp1 = 32 * 4 + 16;
+constexpr int kTabBytes = kGroups * kGrp1;
+// Passes of 2 or more tokens tabulate two tokens to an 8-byte entry: group
+// g's 256-byte table at g * kGrp2, the second pair's tables kPairStride
+// further (16-byte aligned and not a multiple of 512, so the compiler keeps
+// the two pairs' reads apart instead of fusing them into one 16-byte read
+// that it then waits on read by read).
+constexpr int kGrp2 = 32 * 8 + 16;
+constexpr int kPairTab = kGroups * kGrp2;
 constexpr int kPairStride = kPairTab + 16;
-static_assert(kPairStride + kPairTab <= kBufBytes, "two pair tables fit a buffer");
+constexpr int kBufBytes = kPairStride + kPairTab;  // one table buffer
+static_assert(kTabBytes <= kBufBytes && kPairStride % 512 != 0, "table layout");
 
 struct KArgs {
   const uint8_t* w;
@@ -259,8 +265,8 @@ __device__ __forceinline__ void block_dot_pairs(const char* tab, const Block& bl
       const uint32_t ou = __builtin_amdgcn_ubfe(cu, 8 * j, 8);
 #pragma unroll
       for (int p = 0; p < kNP; ++p) {
-        vl[j][p] = *reinterpret_cast<const float2*>(tab + ol + (p * kPairStride + (8 * w + j) * 256));
-        vu[j][p] = *reinterpret_cast<const float2*>(tab + ou + (p * kPairStride + (8 * w + 4 + j) * 256));
+        vl[j][p] = *reinterpret_cast<const float2*>(tab + ol + (p * kPairStride + (8 * w + j) * kGrp2));
+        vu[j][p] = *reinterpret_cast<const float2*>(tab + ou + (p * kPairStride + (8 * w + 4 + j) * kGrp2));
       }
     }
 #pragma unroll
@@ -281,6 +287,7 @@ __device__ __forceinline__ void block_dot_pairs(const char* tab, const Block& bl
 // Sum over the 64 groups of one block of table[code], for MC tokens.
 template <int MC>
 __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, float (&acc)[kMT]) {
+  static_assert(MC * kTabBytes <= kBufBytes, "one-token tables of the pass fit a buffer");
   const float d = half_bits_to_float(blk.d16);
   float bs[MC];
 #pragma unroll
@@ -302,8 +309,8 @@ __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, flo
       const uint32_t ou = __builtin_amdgcn_ubfe(cu, 8 * j, 8);
 #pragma unroll
       for (int m = 0; m < MC; ++m) {
-        bs[m] += *reinterpret_cast<const float*>(tab + ol + (m * kTokStride + (8 * w + j) * 128));
-        bs[m] += *reinterpret_cast<const float*>(tab + ou + (m * kTokStride + (8 * w + 4 + j) * 128));
+        bs[m] += *reinterpret_cast<const float*>(tab + ol + (m * kTabBytes + (8 * w + j) * kGrp1));
+        bs[m] += *reinterpret_cast<const float*>(tab + ou + (m * kTabBytes + (8 * w + 4 + j) * kGrp1));
       }
     }
   }
@@ -337,7 +344,7 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
     if (kPair ? m == 2 * m0 : m == 0) tok0 = tok[m];
     if (kPair && m == 2 * m0 + 1) tok1 = tok[m];
   }
-  const int tab_off0 = kPair ? m0 * kPairStride + it_g * 256 + it_z * 64 : it_g * 128 + it_z * 32;
+  const int tab_off0 = kPair ? m0 * kPairStride + it_g * kGrp2 + it_z * 64 : it_g * kGrp1 + it_z * 32;
 
 #pragma unroll
   for (int m = 0; m < kMT; ++m) acc[m] = 0.0f;
