@@ -6,10 +6,10 @@
 //
 // Work unit: a workgroup of 512 threads owns 512 consecutive rows of one
 // expert (one row per thread, eight 64-row tiles) and a range of 256-weight
-// blocks along k, for up to kMT tokens at a time.  The (token, expert) pair
-// list is scanned on the device: the first valid pair of an expert leads and
-// collects every later pair with that expert, so the expert's weights stream
-// once per kMT tokens.
+// blocks along k, for up to kMT tokens at a time (kMT2 on the matrix
+// cores).  The (token, expert) pair list is scanned on the device: the first
+// valid pair of an expert leads and collects every later pair with that
+// expert, so the expert's weights stream once per pass.
 //
 // Inner product per block: a group of four weights holds one of 32 patterns,
 // so for each token and group the 32 possible signed sums of its four
@@ -59,7 +59,8 @@ namespace {
 
 constexpr int kRows = 512;                 // rows (= threads) per workgroup
 constexpr int kWaves = kRows / 64;
-constexpr int kMT = 4;                     // tokens per pass
+constexpr int kMT = 4;                     // tokens per table pass
+constexpr int kMT2 = 2 * kMT;              // tokens per matrix-core pass
 // One-token passes: group g's 128-byte table at g * kGrp1.
 constexpr int kGrp1 = 32 * 4 + 16;
 constexpr int kTabBytes = kGroups * kGrp1;
@@ -108,8 +109,8 @@ struct Shared {
   // 128 bytes apart are bank-conflict free whatever the codes)
   uint32_t lut[64];
   alignas(16) char tab[2][kBufBytes];       // two table buffers; per token 32 signed sums x 64 groups
-  int pairs[kMT];
-  int toks[kMT];
+  int pairs[kMT2];
+  int toks[kMT2];
   int mc;
   int next;
   int lead;
@@ -120,8 +121,9 @@ struct Shared {
   int wsum[kWaves];
 };
 
-// Collect up to kMT pairs with expert e and a valid token, from `cursor` on,
+// Collect up to kCap pairs with expert e and a valid token, from `cursor` on,
 // in index order.  Leaves the count in sh.mc and the resume index in sh.next.
+template <int kCap>
 __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) {
@@ -142,9 +144,9 @@ __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
     if (tid == 0) {
       int mc = sh.mc;
       int next = base + kRows;
-      for (int w = 0; w < kWaves && mc < kMT; ++w) {
+      for (int w = 0; w < kWaves && mc < kCap; ++w) {
         unsigned long long bm = sh.ball[w];
-        while (bm != 0ull && mc < kMT) {
+        while (bm != 0ull && mc < kCap) {
           const int bit = __ffsll(static_cast<long long>(bm)) - 1;
           bm &= bm - 1ull;
           const int qq = base + 64 * w + bit;
@@ -154,14 +156,14 @@ __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
           next = qq + 1;
         }
       }
-      if (mc < kMT) next = base + kRows;
+      if (mc < kCap) next = base + kRows;
       sh.mc = mc;
       sh.next = next;
       // unused token slots repeat the last token found (a 3-token pass may run as a 4-token one)
-      for (int m = mc; m < kMT; ++m) sh.toks[m] = mc > 0 ? sh.toks[mc - 1] : 0;
+      for (int m = mc; m < kCap; ++m) sh.toks[m] = mc > 0 ? sh.toks[mc - 1] : 0;
     }
     __syncthreads();
-    if (sh.mc >= kMT) break;
+    if (sh.mc >= kCap) break;
   }
 }
 
@@ -417,7 +419,7 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// One block of this thread's row for the pass's four tokens on the matrix
+// One block of this thread's row for a set of four tokens on the matrix
 // cores.  v_mfma_f32_4x4x4_16b_bf16 multiplies 16 independent 4x4 blocks;
 // here block b is the wavefront's row quad 4b..4b+3 and k is one group: the B
 // operand of lane l is row l's four weights of the group (a pattern read
@@ -427,7 +429,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // s = 0..3, so four 8-byte reads per block fetch all 64 groups.  Lane l's
 // four results are row l for tokens 0..3.  Products of bf16 values are exact
 // in fp32; the group sums accumulate in fp32 (even and odd groups apart),
-// then the block's d scales them (one FMA per token), as in block_dot.
+// then the block's d scales them (one FMA per token), as in block_dot.  A
+// pass of 5-8 tokens runs two sets on the same pattern reads, so the
+// weights stream once for eight tokens.
 // Group G's product: the activations of group G (block G % 16 of the set
 // G / 16) broadcast to all 16 blocks.  abid must be an immediate, hence the
 // template.
@@ -459,74 +463,90 @@ __device__ __forceinline__ void word_patterns(const Block& blk, const char* lb, 
   }
 }
 
-// The MFMAs of code word W: its low-nibble groups into c0, high into c1.
-template <int W>
-__device__ __forceinline__ void word_mfmas(const s16x4_t (&xa)[4], const s16x4_t (&bl)[4], const s16x4_t (&bu)[4],
-                                           f32x4_t& c0, f32x4_t& c1) {
-  c0 = mfma_group<8 * W + 0>(xa, bl[0], c0);
-  c1 = mfma_group<8 * W + 4>(xa, bu[0], c1);
-  c0 = mfma_group<8 * W + 1>(xa, bl[1], c0);
-  c1 = mfma_group<8 * W + 5>(xa, bu[1], c1);
-  c0 = mfma_group<8 * W + 2>(xa, bl[2], c0);
-  c1 = mfma_group<8 * W + 6>(xa, bu[2], c1);
-  c0 = mfma_group<8 * W + 3>(xa, bl[3], c0);
-  c1 = mfma_group<8 * W + 7>(xa, bu[3], c1);
+// The MFMAs of code word W for each token set: its low-nibble groups into
+// c[t][0], high into c[t][1] (the same instruction order for every set, so a
+// token's result does not depend on the set it is in).
+template <int W, int kSets>
+__device__ __forceinline__ void word_mfmas(const s16x4_t (&xa)[kSets][4], const s16x4_t (&bl)[4],
+                                           const s16x4_t (&bu)[4], f32x4_t (&c)[kSets][2]) {
+#pragma unroll
+  for (int t = 0; t < kSets; ++t) {
+    c[t][0] = mfma_group<8 * W + 0>(xa[t], bl[0], c[t][0]);
+    c[t][1] = mfma_group<8 * W + 4>(xa[t], bu[0], c[t][1]);
+    c[t][0] = mfma_group<8 * W + 1>(xa[t], bl[1], c[t][0]);
+    c[t][1] = mfma_group<8 * W + 5>(xa[t], bu[1], c[t][1]);
+    c[t][0] = mfma_group<8 * W + 2>(xa[t], bl[2], c[t][0]);
+    c[t][1] = mfma_group<8 * W + 6>(xa[t], bu[2], c[t][1]);
+    c[t][0] = mfma_group<8 * W + 3>(xa[t], bl[3], c[t][0]);
+    c[t][1] = mfma_group<8 * W + 7>(xa[t], bu[3], c[t][1]);
+  }
 }
 
 // Words W and up: the pattern reads of word W+1 are issued before the MFMAs
 // of word W, so the reads of one word are in flight while the previous
 // word's products run.
-template <int W>
-__device__ __forceinline__ void words_from(const Block& blk, const char* lb, const s16x4_t (&xa)[4],
-                                           s16x4_t (&bl)[4], s16x4_t (&bu)[4], f32x4_t& c0, f32x4_t& c1) {
+template <int W, int kSets>
+__device__ __forceinline__ void words_from(const Block& blk, const char* lb, const s16x4_t (&xa)[kSets][4],
+                                           s16x4_t (&bl)[4], s16x4_t (&bu)[4], f32x4_t (&c)[kSets][2]) {
   if constexpr (W < 7) {
     s16x4_t nl[4], nu[4];
     word_patterns<W + 1>(blk, lb, nl, nu);
-    word_mfmas<W>(xa, bl, bu, c0, c1);
-    words_from<W + 1>(blk, lb, xa, nl, nu, c0, c1);
+    word_mfmas<W, kSets>(xa, bl, bu, c);
+    words_from<W + 1, kSets>(blk, lb, xa, nl, nu, c);
   } else {
-    word_mfmas<W>(xa, bl, bu, c0, c1);
+    word_mfmas<W, kSets>(xa, bl, bu, c);
   }
 }
 
+// One block for kSets sets of four tokens; set t's activations are staged
+// 2048 bytes after set t-1's.  The pattern reads serve every set.
+template <int kSets>
 __device__ __forceinline__ void block_mfma(const char* xs, const uint32_t* lut, const Block& blk, int lane,
-                                           float (&acc)[kMT]) {
+                                           float (&acc)[kMT * kSets]) {
   const float d = half_bits_to_float(blk.d16);
-  s16x4_t xa[4];
+  s16x4_t xa[kSets][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const s16x4_t*>(xs + (64 * s + lane) * 8);
-  f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < kSets; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xa[t][s] = *reinterpret_cast<const s16x4_t*>(xs + t * 2048 + (64 * s + lane) * 8);
+  f32x4_t c[kSets][2];
+#pragma unroll
+  for (int t = 0; t < kSets; ++t) c[t][0] = c[t][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const char* lb = reinterpret_cast<const char*>(lut);
   s16x4_t bl[4], bu[4];
   word_patterns<0>(blk, lb, bl, bu);
-  words_from<0>(blk, lb, xa, bl, bu, c0, c1);
+  words_from<0, kSets>(blk, lb, xa, bl, bu, c);
 #pragma unroll
-  for (int m = 0; m < kMT; ++m) acc[m] = fmaf(d, c0[m] + c1[m], acc[m]);
+  for (int t = 0; t < kSets; ++t)
+#pragma unroll
+    for (int m = 0; m < kMT; ++m) acc[kMT * t + m] = fmaf(d, c[t][0][m] + c[t][1][m], acc[kMT * t + m]);
 }
 
 // Blocks [b_begin, b_end) of this workgroup's rows for bf16 activations and
-// up to four tokens on the matrix cores (token slots past the pass's count
-// repeat its last token; their results are not stored).  The pipeline is
-// run_chunk's: weights one block ahead, activations two; each block's
-// activations (4 tokens x 64 groups x 8 bytes) are staged in LDS in
-// [group][token] order while the previous block is multiplied.
+// up to 4 * kSets tokens on the matrix cores (token slots past the pass's
+// count repeat its last token; their results are not stored).  The pipeline
+// is run_chunk's: weights one block ahead, activations two; each block's
+// activations (4 tokens x 64 groups x 8 bytes per set) are staged in LDS in
+// [set][group][token] order while the previous block is multiplied.
+template <int kSets>
 __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const uint8_t* wexp, int b_begin,
-                                               int b_end, float (&acc)[kMT]) {
+                                               int b_end, float (&acc)[kMT * kSets]) {
+  constexpr int kTok = kMT * kSets;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // staging item of this thread (threads 0..255): token tid >> 6, group tid & 63
+  // staging item of this thread (threads 0..64 * kTok - 1): token tid >> 6, group tid & 63
   const int st_m = tid >> 6, st_g = tid & 63;
-  const bool stages = tid < 4 * 64;
+  const bool stages = tid < kTok * 64;
   int tok_st = 0;
 #pragma unroll
-  for (int m = 0; m < kMT; ++m) {
+  for (int m = 0; m < kTok; ++m) {
     const int t = __builtin_amdgcn_readfirstlane(sh.toks[m]);
     if (m == st_m) tok_st = t;
   }
-  const int st_off = (st_g * 4 + st_m) * 8;
+  const int st_off = (st_m >> 2) * 2048 + (st_g * 4 + (st_m & 3)) * 8;
 
 #pragma unroll
-  for (int m = 0; m < kMT; ++m) acc[m] = 0.0f;
+  for (int m = 0; m < kTok; ++m) acc[m] = 0.0f;
 
   const int rowbase = blockIdx.x * kRows + wave * 64;
   const int valid = max(0, min(kTileRows, a.n - rowbase));
@@ -541,7 +561,7 @@ __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const
     const uint32_t off = b < b_end ? (static_cast<uint32_t>(b) * valid + lane) * kBlockBytes : tile_bytes;
     load_raw_block(rs, off, r);
   };
-  // every thread loads (threads 256.. load token 0's group and stage nothing)
+  // every thread loads (threads that stage nothing load token 0's group)
   auto load_x = [&](XGroup<kXBF16>& x, int b) { x.load(a, tok_st, static_cast<int64_t>(b) * kQK + 4 * st_g); };
   auto stage = [&](const XGroup<kXBF16>& x, char* t) {
     if (stages) *reinterpret_cast<uint2*>(t + st_off) = make_uint2(x.v[0], x.v[1]);
@@ -561,7 +581,7 @@ __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const
     if (b + 1 < b_end) stage(xn, tnext);
     __builtin_amdgcn_sched_barrier(0);
     load_x(xn, min(b + 2, b_end - 1));
-    block_mfma(tcur, sh.lut, blk, lane, acc);
+    block_mfma<kSets>(tcur, sh.lut, blk, lane, acc);
     __syncthreads();  // block b+1's activations are staged and every thread is done with block b's
   };
   {
@@ -738,30 +758,40 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
 
   int cursor = p;
   for (;;) {
-    gather(a, sh, e, cursor);
+    gather<kMfma ? kMT2 : kMT>(a, sh, e, cursor);
     const int mc = __builtin_amdgcn_readfirstlane(sh.mc);
     if (mc == 0) break;
     cursor = __builtin_amdgcn_readfirstlane(sh.next);
-    float acc[kMT];
-    if (kMfma && mc >= kMfmaMinTokens) {
-      run_chunk_mfma(a, sh, wexp, b_begin, b_end, acc);
-    } else switch (mc) {
-      case 1: run_chunk<kMode, 1>(a, sh, wexp, b_begin, b_end, acc); break;
-      case 2: run_chunk<kMode, 2>(a, sh, wexp, b_begin, b_end, acc); break;
-      case 3:  // pair tables take 3 tokens as 4 (the fourth repeats the third, its sums unused)
-        run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc);
-        break;
-      default: run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc); break;
-    }
-    if (row_ok) {
+    auto store = [&](const auto& acc) {
+      constexpr int kN = sizeof(acc) / sizeof(float);
+      if (row_ok) {
 #pragma unroll
-      for (int m = 0; m < kMT; ++m) {
-        if (m < mc) {
-          const int64_t q = sh.pairs[m];
-          if (n_slots == 1) a.y[q * a.n + row] = acc[m];
-          else a.partial[(static_cast<int64_t>(slot) * a.n_pairs + q) * a.n + row] = acc[m];
+        for (int m = 0; m < kN; ++m) {
+          if (m < mc) {
+            const int64_t q = sh.pairs[m];
+            if (n_slots == 1) a.y[q * a.n + row] = acc[m];
+            else a.partial[(static_cast<int64_t>(slot) * a.n_pairs + q) * a.n + row] = acc[m];
+          }
         }
       }
+    };
+    if (kMfma && mc > kMT) {
+      float acc[kMT2];
+      run_chunk_mfma<2>(a, sh, wexp, b_begin, b_end, acc);
+      store(acc);
+    } else {
+      float acc[kMT];
+      if (kMfma && mc >= kMfmaMinTokens) {
+        run_chunk_mfma<1>(a, sh, wexp, b_begin, b_end, acc);
+      } else switch (mc) {
+        case 1: run_chunk<kMode, 1>(a, sh, wexp, b_begin, b_end, acc); break;
+        case 2: run_chunk<kMode, 2>(a, sh, wexp, b_begin, b_end, acc); break;
+        case 3:  // pair tables take 3 tokens as 4 (the fourth repeats the third, its sums unused)
+          run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc);
+          break;
+        default: run_chunk<kMode, 4>(a, sh, wexp, b_begin, b_end, acc); break;
+      }
+      store(acc);
     }
     // the reduction learns each pair's part count from the first unit of its expert
     if (a.pair_sub && split == 0 && sub == 0 && blockIdx.x == 0 && tid < mc) a.pair_sub[sh.pairs[tid]] = nsub;
@@ -848,17 +878,18 @@ int cus_of_current_device() {
   return cus_of_device(dev);
 }
 
-// Work of one pass over a block, relative to a one-token pass, for a pass
-// of 1..4 tokens (measured with bf16 activations on a full layer, every
-// expert given the same token count): on the tables 1, 1.45, 2.1 and 2.18;
-// in the kernel variant with the matrix-core form (3 and 4 tokens there)
-// 1, 1.2, 1.4 and 1.47.  An expert with m tokens makes floor(m / 4)
-// four-token passes and one pass of the rest.
+// Work of one pass over a block, relative to a one-token pass, measured on
+// a full layer with every expert given the same token count: on the tables
+// (passes of 1..4 tokens) 1, 1.45, 2.1 and 2.18; in the kernel variant with
+// the matrix-core form (passes of 1..8 tokens, 3 and more on the matrix
+// cores) 1, 1.19, 1.47, 1.52, 2.03, 2.12, 2.2 (interpolated) and 2.31.  An
+// expert with m tokens makes floor(m / P) full passes of P tokens and one
+// pass of the rest.
 static double block_cost(int m, bool mfma) {
   constexpr double kTab[5] = {0.0, 1.0, 1.45, 2.1, 2.18};
-  constexpr double kMat[5] = {0.0, 1.0, 1.2, 1.4, 1.47};
-  const double* c = mfma ? kMat : kTab;
-  return (m / 4) * c[4] + c[m % 4];
+  constexpr double kMat[9] = {0.0, 1.0, 1.19, 1.47, 1.52, 2.03, 2.12, 2.2, 2.31};
+  if (mfma) return (m / kMT2) * kMat[kMT2] + kMat[m % kMT2];
+  return (m / kMT) * kTab[kMT] + kTab[m % kMT];
 }
 
 // The matrix-core variant pays off once experts commonly hold 3 or more of

@@ -195,10 +195,11 @@ def test_gemv_plan_ignores_malformed_overrides(L, monkeypatch, env):
 
 def test_gemv_plan_parts_need_the_leader_table(L, monkeypatch):
     """Experts are parted only while the workgroup's table space can rank
-    them (8208 experts); beyond, each expert is one unit even when forced."""
+    them (8708 experts: two 34832-byte table buffers of int pairs); beyond,
+    each expert is one unit even when forced."""
     monkeypatch.setenv("STQ_GEMV_PLAN", "1,3")
-    assert _plan(L, ne=8208, np_=64)[1][:2] == (1, 3)
-    assert _plan(L, ne=8209, np_=64) == (0, (1, 1, 0))
+    assert _plan(L, ne=8708, np_=64)[1][:2] == (1, 3)
+    assert _plan(L, ne=8709, np_=64) == (0, (1, 1, 0))
     monkeypatch.setenv("STQ_GEMV_PLAN", "4,3")
     assert _plan(L, ne=9000, np_=64) == (0, (4, 1, _scratch(4, 1, 64, 4096)))
 

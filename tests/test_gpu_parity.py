@@ -265,14 +265,14 @@ def test_gemv_token_parts_match_oracle(stq, monkeypatch, plan):
                     f"plan {plan} pair {i} (expert {e})")
 
 
-def _pass_sizes(pe):
+def _pass_sizes(pe, per_pass):
     """Tokens in the pass that serves each pair: an expert's pairs are taken in
-    pair order, four to a pass."""
+    pair order, per_pass to a pass."""
     size = np.zeros(pe.size, dtype=int)
     for e in np.unique(pe):
         idx = np.flatnonzero(pe == e)
-        for c in range(0, idx.size, 4):
-            size[idx[c:c + 4]] = min(4, idx.size - c)
+        for c in range(0, idx.size, per_pass):
+            size[idx[c:c + per_pass]] = min(per_pass, idx.size - c)
     return size
 
 
@@ -281,20 +281,22 @@ def _pass_sizes(pe):
 def test_gemv_pair_result_does_not_depend_on_its_companions(stq, monkeypatch, plan, xdt):
     """Under a plan that does not part experts by token count, a pair's output
     does not depend on the other pairs batched with it, as long as its pass
-    runs on the same form.  Experts hold 1-8 tokens (passes of 1-4).
-    Passes of 1-2 tokens run on the tables (two-token tables have the sums
-    and per-token order of adds of one-token tables), so such a pair equals
-    the pair computed alone (a one-token pass) bit for bit; fp32 activations
-    always take the tables.  In the bf16 call (as many pairs as experts or
-    more, so the matrix-core kernel variant) passes of 3-4 tokens run on the
-    matrix cores, where a token's results use only its own activations: such
-    a pair equals the same pair in a second call with the pairs in another
-    order (other companions), bit for bit, where it again sits in a pass of
-    3-4 tokens."""
+    runs on the same form.  Experts hold 1-8, 10 and 11 tokens.  Table
+    passes take up to 4 tokens, matrix-core passes up to 8.  Passes of 1-2
+    tokens run on the tables (two-token tables have the sums and per-token
+    order of adds of one-token tables), so such a pair equals the pair
+    computed alone (a one-token pass) bit for bit; fp32 activations always
+    take the tables, in passes of up to 4.  In the bf16 call (as many pairs
+    as experts or more, so the matrix-core kernel variant) passes of 3-8
+    tokens run on the matrix cores, where a token's results use only its own
+    activations and every set of four tokens runs the same instructions:
+    such a pair equals the same pair in a second call with the pairs in
+    another order (other companions), bit for bit, where it again sits in a
+    pass of 3-8 tokens."""
     monkeypatch.setenv("STQ_GEMV_PLAN", plan)
     rng = np.random.default_rng(63)
-    counts = [1, 2, 3, 4, 5, 6, 7, 8]
-    n_experts, n, k, n_tokens = len(counts), 320, 2560, 10
+    counts = [1, 2, 3, 4, 5, 6, 7, 8, 10, 11]
+    n_experts, n, k, n_tokens = len(counts), 320, 2560, 12
     rb = O.row_bytes(k)
     table = np.concatenate([O.quantize_rows(S.gaussian_weights(900 + e, n, k), None).reshape(-1)
                             for e in range(n_experts)])
@@ -306,7 +308,8 @@ def test_gemv_pair_result_does_not_depend_on_its_companions(stq, monkeypatch, pl
     x = dev(xb.view(np.int16)).view(torch.bfloat16) if xdt == "bf16" else dev(xf)
     wt = dev(table)
     y = host(stq.gemv(wt, n * rb, n_experts, n, k, x, dev(pe), dev(pt)))
-    size = _pass_sizes(pe)
+    per_pass = 8 if xdt == "bf16" else 4
+    size = _pass_sizes(pe, per_pass)
     matrix = (size >= 3) if xdt == "bf16" else np.zeros(pe.size, bool)
     for i in np.flatnonzero(~matrix):
         yi = host(stq.gemv(wt, n * rb, n_experts, n, k, x, dev(pe[i:i + 1]), dev(pt[i:i + 1])))
@@ -314,7 +317,7 @@ def test_gemv_pair_result_does_not_depend_on_its_companions(stq, monkeypatch, pl
     if matrix.any():
         order = rng.permutation(pe.size)
         y2 = host(stq.gemv(wt, n * rb, n_experts, n, k, x, dev(pe[order]), dev(pt[order])))
-        size2 = _pass_sizes(pe[order])
+        size2 = _pass_sizes(pe[order], per_pass)
         checked = 0
         for j, i in enumerate(order):
             if matrix[i] and size2[j] >= 3:
