@@ -350,6 +350,9 @@ __device__ __forceinline__ void run_chunk(const KArgs& a, Shared& sh, const uint
 
 #pragma unroll
   for (int m = 0; m < kMT; ++m) acc[m] = 0.0f;
+  // an empty part (uniform over the workgroup) adds zeros; the loads below
+  // assume b_begin < b_end
+  if (b_begin >= b_end) return;
 
   // this wavefront's rows are one tile of the packed matrix
   const int rowbase = blockIdx.x * kRows + wave * 64;
@@ -547,6 +550,7 @@ __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const
 
 #pragma unroll
   for (int m = 0; m < kTok; ++m) acc[m] = 0.0f;
+  if (b_begin >= b_end) return;  // an empty part, as in run_chunk
 
   const int rowbase = blockIdx.x * kRows + wave * 64;
   const int valid = max(0, min(kTileRows, a.n - rowbase));
