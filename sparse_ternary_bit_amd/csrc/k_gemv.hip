@@ -123,48 +123,48 @@ struct Shared {
 
 // Collect up to kCap pairs with expert e and a valid token, from `cursor` on,
 // in index order.  Leaves the count in sh.mc and the resume index in sh.next.
+// Each matching thread places its own pair and token at its rank among the
+// matches (a prefix count over the wavefronts' ballots), so no thread loads
+// the pairs one after another.
 template <int kCap>
 __device__ void gather(const KArgs& a, Shared& sh, int e, int cursor) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) {
-    sh.mc = 0;
-    sh.next = a.n_pairs;
-  }
-  __syncthreads();
-  for (int base = cursor; base < a.n_pairs; base += kRows) {
+  int mc = 0;  // pairs found so far, the same in every thread
+  for (int base = cursor; base < a.n_pairs && mc < kCap; base += kRows) {
     const int q = base + tid;
     bool match = false;
+    int tq = 0;
     if (q < a.n_pairs) {
-      const int tq = pair_token(a, q);
+      tq = pair_token(a, q);
       match = pair_expert(a, q) == e && tq >= 0 && tq < a.n_tokens;
     }
     const unsigned long long bal = __ballot(match);
     if (lane == 0) sh.ball[wave] = bal;
     __syncthreads();
-    if (tid == 0) {
-      int mc = sh.mc;
-      int next = base + kRows;
-      for (int w = 0; w < kWaves && mc < kCap; ++w) {
-        unsigned long long bm = sh.ball[w];
-        while (bm != 0ull && mc < kCap) {
-          const int bit = __ffsll(static_cast<long long>(bm)) - 1;
-          bm &= bm - 1ull;
-          const int qq = base + 64 * w + bit;
-          sh.pairs[mc] = qq;
-          sh.toks[mc] = pair_token(a, qq);
-          ++mc;
-          next = qq + 1;
-        }
-      }
-      if (mc < kCap) next = base + kRows;
-      sh.mc = mc;
-      sh.next = next;
-      // unused token slots repeat the last token found (a 3-token pass may run as a 4-token one)
-      for (int m = mc; m < kCap; ++m) sh.toks[m] = mc > 0 ? sh.toks[mc - 1] : 0;
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = __popcll(sh.ball[w]);
+      before += (w < wave) ? c : 0;
+      total += c;
     }
-    __syncthreads();
-    if (sh.mc >= kCap) break;
+    const int slot = mc + before + __popcll(bal & ((1ull << lane) - 1ull));
+    if (match && slot < kCap) {
+      sh.pairs[slot] = q;
+      sh.toks[slot] = tq;
+      // the pass is full: the next one resumes after its last pair
+      if (slot == kCap - 1) sh.next = q + 1;
+    }
+    mc = min(kCap, mc + total);
+    __syncthreads();  // sh.ball is rewritten by the next chunk; the slots are visible
   }
+  if (tid == 0) {
+    sh.mc = mc;
+    if (mc < kCap) sh.next = a.n_pairs;  // every remaining pair was scanned
+    // unused token slots repeat the last token found (a 3-token pass may run as a 4-token one)
+    for (int m = mc; m < kCap; ++m) sh.toks[m] = mc > 0 ? sh.toks[mc - 1] : 0;
+  }
+  __syncthreads();
 }
 
 // Activations of one group (4 values) of one token at column `col`, by
