@@ -209,6 +209,38 @@ def test_gemv_many_pairs_one_expert(stq):
         check_close(y[t], y_ref[t], A, GEMV_TOL, f"token {t}")
 
 
+@pytest.mark.parametrize("plan", [None, "1,1", "3,2"])
+def test_gemv_matrix_core_passes_of_5_to_16_tokens(stq, monkeypatch, plan):
+    """bf16 activations with at least as many pairs as experts take the
+    matrix-core kernel: experts with 5-8 tokens run one pass of two token
+    sets, 12 and 16 tokens two passes (8 + 4, 8 + 8), next to experts with
+    1-3 tokens on the tables; ragged n (not a multiple of 64), several
+    blocks, pairs interleaved across experts.  Every output element within
+    1e-3 * A of the oracle."""
+    if plan:
+        monkeypatch.setenv("STQ_GEMV_PLAN", plan)
+    else:
+        monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    rng = np.random.default_rng(64)
+    counts = [5, 6, 7, 8, 12, 16, 1, 2, 3]
+    n_experts, n, k, n_tokens = len(counts), 200, 1536, 16
+    rb = O.row_bytes(k)
+    table = np.concatenate([O.quantize_rows(S.gaussian_weights(1100 + e, n, k), None).reshape(-1)
+                            for e in range(n_experts)])
+    pe = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    pt = np.concatenate([rng.choice(n_tokens, c, replace=False) for c in counts]).astype(np.int32)
+    perm = rng.permutation(pe.size)
+    pe, pt = pe[perm], pt[perm]
+    assert pe.size >= n_experts
+    xb, xf = S.bf16_normal(rng, (n_tokens, k))
+    y = host(stq.gemv(dev(table), n * rb, n_experts, n, k, dev(xb.view(np.int16)).view(torch.bfloat16),
+                      dev(pe), dev(pt)))
+    for i in range(pe.size):
+        raw = table[int(pe[i]) * n * rb:(int(pe[i]) + 1) * n * rb]
+        check_close(y[i], O.gemv(raw, n, k, xf[pt[i]]), O.tolerance_scale(raw, n, k, xf[pt[i]])[0],
+                    GEMV_TOL, f"plan {plan} pair {i} (expert {int(pe[i])}, {counts[int(pe[i])]} tokens)")
+
+
 def test_gemv_wide_batch(stq):
     """512 pairs over 16 experts: shared and distinct experts mixed."""
     n_experts, n, k, n_tokens = 16, 256, 1024, 64
