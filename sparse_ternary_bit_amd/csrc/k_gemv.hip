@@ -94,6 +94,7 @@ struct KArgs {
   float* partial;  // [splits * max_sub, n_pairs, n] when a pair's output is split
   int32_t* pair_sub;  // per pair: its expert's part count (read by the reduction)
   int ppt;         // without pair_token: pair q uses token q / ppt
+  int order;       // number units by cost class (longest first) when the pairs fit one chunk
 };
 
 // bf16 passes of at least this many tokens run on the matrix cores (in the
@@ -631,10 +632,13 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int* first = reinterpret_cast<int*>(&sh.tab[0][0]);
   int* count = first + a.n_experts;
-  const bool parts = a.max_sub > 1;  // else every leading pair is one unit and counts are not needed
+  const bool parts = a.max_sub > 1;  // else every leading pair is one unit
+  // pair counts order the units of one chunk and size an expert's parts
+  const bool ordered = a.order && a.n_pairs <= kRows;
+  const bool counts = parts || ordered;
   for (int e = tid; e < a.n_experts; e += kRows) {
     first[e] = 0x7FFFFFFF;
-    if (parts) count[e] = 0;
+    if (counts) count[e] = 0;
   }
   if (tid == 0) sh.lead = -1;
   __syncthreads();
@@ -642,10 +646,58 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
     int e;
     if (pair_valid(a, q, e)) {
       atomicMin(&first[e], q);
-      if (parts) atomicAdd(&count[e], 1);
+      if (counts) atomicAdd(&count[e], 1);
     }
   }
   __syncthreads();
+  if (ordered) {
+    // One chunk of pairs, more units than resident workgroups: units are
+    // numbered by cost class, the longest
+    // first, so that the last workgroups to start are short ones: whole
+    // experts with 5+, 3-4, 2, 1 tokens, then the parts of parted experts
+    // (each a fraction of its expert's k range).  Within a class, leading
+    // pairs in pair order.  A lane's units (at most kMaxSub = 8) are summed
+    // bit by bit over ballots; a wavefront's five class totals are packed 10
+    // bits apiece (at most as many units as pairs, so at most 512).
+    const int q = tid;
+    int e = -1;
+    const bool lead = q < a.n_pairs && pair_valid(a, q, e) && first[e] == q;
+    const int m = lead ? count[e] : 0;
+    const int units = lead ? (parts ? min(m, a.max_sub) : 1) : 0;
+    const int cls = units > 1 ? 4 : m >= 5 ? 0 : m >= 3 ? 1 : m == 2 ? 2 : 3;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int nbits = parts ? 4 : 1;
+    int lane_before = 0;               // units of earlier lanes of this lane's class
+    unsigned long long wave_tot = 0;   // the wavefront's class totals, packed
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+      for (int b = 0; b < nbits; ++b) {
+        const unsigned long long bal = __ballot(cls == c && ((units >> b) & 1));
+        if (cls == c) lane_before += __popcll(bal & below) << b;
+        wave_tot += static_cast<unsigned long long>(__popcll(bal)) << (10 * c + b);
+      }
+    }
+    if (lane == 0) sh.ball[wave] = wave_tot;
+    __syncthreads();
+    unsigned long long before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const unsigned long long sw = sh.ball[w];
+      before += (w < wave) ? sw : 0ull;
+      total += sw;
+    }
+    int first_unit = static_cast<int>((before >> (10 * cls)) & 1023u) + lane_before;
+    for (int c = 0; c < cls; ++c) first_unit += static_cast<int>((total >> (10 * c)) & 1023u);
+    if (units > 0 && z >= first_unit && z < first_unit + units) {
+      sh.lead = q;
+      sh.sub = z - first_unit;
+      sh.nsub = units;
+    }
+    __syncthreads();  // sh.ball is read above and rewritten by the gather; sh.lead is visible
+    return sh.lead;
+  }
+  // more pairs than one chunk, or all units resident at once: units in
+  // leading-pair order
   int base = 0;
   for (int c = 0; c < a.n_pairs && base <= z; c += kRows) {
     const int q = c + tid;
@@ -1017,6 +1069,9 @@ GemvPlan plan_gemv(const GemvArgs& a, int cus) {
     }
   }
   pl.mfma = use_mfma(a);
+  // order matters only when not every workgroup of the grid is resident at once
+  const int64_t ntiles = (a.n + kRows - 1) / kRows;
+  pl.order_units = a.n_pairs * ntiles * best_splits > 2ll * cus;
   pl.blocks_per_split = best_bps;
   pl.splits = best_splits;
   pl.max_sub = best_sub;
@@ -1066,6 +1121,7 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
   a.partial = static_cast<float*>(partial);
   a.pair_sub = pair_sub_of(pl, partial);
   a.ppt = ga.pairs_per_token > 0 ? static_cast<int>(ga.pairs_per_token) : 1;
+  a.order = pl.order_units ? 1 : 0;
   const int ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
   const dim3 grid(ntiles, pl.splits, a.n_pairs);
   switch (ga.x_mode) {

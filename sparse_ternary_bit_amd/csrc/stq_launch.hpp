@@ -39,6 +39,7 @@ struct GemvPlan {
   int64_t partial_floats;
   int64_t partial_bytes;
   bool mfma;           // bf16 passes of 3+ tokens on the matrix cores (kernel variant)
+  bool order_units;    // more workgroups than resident slots: number units longest first
 };
 // cus: compute units the plan is made for (see cus_of_stream).
 GemvPlan plan_gemv(const GemvArgs& a, int cus);
