@@ -608,13 +608,15 @@ __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const
 // pairs (gather above).  An expert with m pairs is served by min(m, max_sub)
 // units, each taking one part of the workgroup's k range for all m tokens,
 // so a unit costs about what a one-token expert costs whatever m is.  Units
-// are numbered by leading pair in pair order (an expert's parts in k order)
-// and workgroup z serves unit z, so the workgroups with work are the first
-// ones launched whatever the order of the pairs: workgroups are dealt to the
-// shader engines of an XCD round robin, and a periodic pattern of idle
-// workgroups (pairs sorted by expert, say, with four pairs per expert) would
-// otherwise put all the work on one of them.  There are at most as many
-// units as valid pairs, so a grid of n_pairs workgroups covers them.
+// are numbered by leading pair in pair order (an expert's parts in k order;
+// by cost class first when the grid exceeds the resident workgroups, see
+// find_unit) and workgroup z serves unit z, so the workgroups with work are
+// the first ones launched whatever the order of the pairs: workgroups are
+// dealt to the shader engines of an XCD round robin, and a periodic pattern
+// of idle workgroups (pairs sorted by expert, say, with four pairs per
+// expert) would otherwise put all the work on one of them.  There are at
+// most as many units as valid pairs and at most max_sub per expert, so a
+// grid that deep covers them.
 constexpr int kLeadExperts = static_cast<int>(sizeof(Shared::tab) / (2 * sizeof(int)));
 
 __device__ __forceinline__ bool pair_valid(const KArgs& a, int q, int& e) {
@@ -785,11 +787,15 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
     sh.lut[c] = bf(0) | (bf(1) << 16);
     sh.lut[32 + c] = bf(2) | (bf(3) << 16);
   }
-  // an invalid pair z gets a row of NaN, whichever workgroup leads below
-  {
-    const int ez = pair_expert(a, z), tz = pair_token(a, z);
-    if ((ez < 0 || ez >= a.n_experts || tz < 0 || tz >= a.n_tokens) && split == 0 && row_ok)
-      a.y[static_cast<int64_t>(z) * a.n + row] = __builtin_nanf("");
+  // an invalid pair gets a row of NaN, whichever workgroup leads below:
+  // workgroup z marks pairs z, z + gridDim.z, ... (the grid is no deeper
+  // than the units can be)
+  if (split == 0 && row_ok) {
+    for (int q = z; q < a.n_pairs; q += gridDim.z) {
+      const int eq = pair_expert(a, q), tq = pair_token(a, q);
+      if (eq < 0 || eq >= a.n_experts || tq < 0 || tq >= a.n_tokens)
+        a.y[static_cast<int64_t>(q) * a.n + row] = __builtin_nanf("");
+    }
   }
   // this workgroup serves unit z: part `sub` of `nsub` of the expert of leading pair p
   // (uniform; p = -1 if there are fewer units)
@@ -1123,7 +1129,12 @@ hipError_t launch_gemv(const GemvArgs& ga, const GemvPlan& pl, void* partial, hi
   a.ppt = ga.pairs_per_token > 0 ? static_cast<int>(ga.pairs_per_token) : 1;
   a.order = pl.order_units ? 1 : 0;
   const int ntiles = static_cast<int>((ga.n + kRows - 1) / kRows);
-  const dim3 grid(ntiles, pl.splits, a.n_pairs);
+  // units: at most one per valid pair, and with the leader table at most
+  // max_sub per expert; beyond it workgroup z serves pair z
+  const int64_t units = a.n_experts <= kLeadExperts
+                            ? std::min<int64_t>(a.n_pairs, static_cast<int64_t>(a.n_experts) * pl.max_sub)
+                            : a.n_pairs;
+  const dim3 grid(ntiles, pl.splits, static_cast<unsigned>(units));
   switch (ga.x_mode) {
     case kXBF16:
       if (pl.mfma) hipLaunchKernelGGL((gemv_kernel<kXBF16, true>), grid, dim3(kRows), 0, s, a);
