@@ -799,11 +799,19 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
   }
   // this workgroup serves unit z: part `sub` of `nsub` of the expert of leading pair p
   // (uniform; p = -1 if there are fewer units)
-  const int p = __builtin_amdgcn_readfirstlane(a.n_experts <= kLeadExperts ? find_unit(a, sh, z)
-                                                                             : leader_if_first(a, sh, z));
+  // one pair (a single-expert call): it is the only unit and its expert's
+  // only pair, so neither the unit search nor the pair scan is needed
+  const bool single = a.n_pairs == 1;
+  int p;
+  if (single) {
+    int e0;
+    p = __builtin_amdgcn_readfirstlane(pair_valid(a, 0, e0) ? 0 : -1);
+  } else {
+    p = __builtin_amdgcn_readfirstlane(a.n_experts <= kLeadExperts ? find_unit(a, sh, z) : leader_if_first(a, sh, z));
+  }
   if (p < 0) return;
   const int e = __builtin_amdgcn_readfirstlane(pair_expert(a, p));
-  const bool parts = a.max_sub > 1;
+  const bool parts = a.max_sub > 1 && !single;
   const int sub = parts ? __builtin_amdgcn_readfirstlane(sh.sub) : 0;
   const int nsub = parts ? __builtin_amdgcn_readfirstlane(sh.nsub) : 1;
 
@@ -820,7 +828,18 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
 
   int cursor = p;
   for (;;) {
-    gather<kMfma ? kMT2 : kMT>(a, sh, e, cursor);
+    if (single) {
+      if (tid == 0) {
+        sh.mc = cursor == 0 ? 1 : 0;
+        sh.next = 1;
+        sh.pairs[0] = 0;
+        const int t0 = pair_token(a, 0);
+        for (int m = 0; m < kMT2; ++m) sh.toks[m] = t0;
+      }
+      __syncthreads();
+    } else {
+      gather<kMfma ? kMT2 : kMT>(a, sh, e, cursor);
+    }
     const int mc = __builtin_amdgcn_readfirstlane(sh.mc);
     if (mc == 0) break;
     cursor = __builtin_amdgcn_readfirstlane(sh.next);
