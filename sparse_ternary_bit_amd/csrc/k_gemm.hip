@@ -126,19 +126,22 @@ __device__ __forceinline__ void run_pass(const GArgs& a, Smem& sh, const uint8_t
 
   // activations, half a block (128 of them, 16 chunks of 16 bytes) per token
   // at a time: 4 tokens per wavefront instruction; chunk c of token t goes to
-  // slot c ^ (t & 15) of the token's 256 bytes
+  // slot c ^ (t & 15) of the token's 256 bytes.  Wavefront w stages
+  // instructions j = w, w + 4, ...: this lane's token t = 4j + lane / 16 moves
+  // by 16 tokens per step and t & 15, so the chunk c, stays the same; tokens
+  // past the pass (t >= mt) read zeros through the range check and are not
+  // stored
   const int n_ins = (mt + 3) >> 2;
   const uint32_t xrow = static_cast<uint32_t>(a.k) * 2;
   const Rsrc xs_rs = make_rsrc(a.x + row0 * a.k, static_cast<uint32_t>(mt) * xrow);
+  const int t_first = 4 * wave + (lane >> 4);
+  const uint32_t x_first = static_cast<uint32_t>(t_first) * xrow + (((lane & 15) ^ (t_first & 15)) * 16);
   auto stage_x = [&](int h, int buf) {
-    for (int j = wave; j < n_ins; j += kWaves) {
-      const int t = 4 * j + (lane >> 4);
-      const int c = (lane & 15) ^ (t & 15);
-      const uint32_t voff = static_cast<uint32_t>(min(t, mt - 1)) * xrow + static_cast<uint32_t>(h) * kHalfBytes + c * 16;
+    uint32_t voff = x_first + static_cast<uint32_t>(h) * kHalfBytes;
+    for (int j = wave; j < n_ins; j += kWaves, voff += 16 * xrow)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xs_rs, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(sh.x[buf] + j * 1024)),
           16, static_cast<int>(voff), 0, 0, 0);
-    }
   };
 
   // the tile run of block b (valid * 42 bytes) into this wavefront's window,
