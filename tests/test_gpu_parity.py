@@ -241,6 +241,33 @@ def test_gemv_matrix_core_passes_of_5_to_16_tokens(stq, monkeypatch, plan):
                     GEMV_TOL, f"plan {plan} pair {i} (expert {int(pe[i])}, {counts[int(pe[i])]} tokens)")
 
 
+@pytest.mark.parametrize("plan", [None, "4,1", "3,3"])
+def test_gemv_single_pair_valid_and_invalid(stq, monkeypatch, plan):
+    """One (token, expert) pair takes the single-pair path (no unit search):
+    a valid pair matches the oracle under planned, split and split-and-parted
+    plans; an unknown expert or token gives a row of NaN."""
+    if plan:
+        monkeypatch.setenv("STQ_GEMV_PLAN", plan)
+    else:
+        monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    n_experts, n, k, n_tokens = 3, 136, 1280, 4
+    rb = O.row_bytes(k)
+    table = np.concatenate([O.quantize_rows(S.gaussian_weights(1300 + e, n, k), None).reshape(-1)
+                            for e in range(n_experts)])
+    xb, xf = S.bf16_normal(np.random.default_rng(65), (n_tokens, k))
+    xt = dev(xb.view(np.int16)).view(torch.bfloat16)
+    for e, t in [(2, 3), (0, 0), (3, 1), (-1, 1), (1, 4), (1, -1)]:
+        pe = dev(np.array([e], dtype=np.int32))
+        pt = dev(np.array([t], dtype=np.int32))
+        y = host(stq.gemv(dev(table), n * rb, n_experts, n, k, xt, pe, pt))
+        if 0 <= e < n_experts and 0 <= t < n_tokens:
+            raw = table[e * n * rb:(e + 1) * n * rb]
+            check_close(y[0], O.gemv(raw, n, k, xf[t]), O.tolerance_scale(raw, n, k, xf[t])[0], GEMV_TOL,
+                        f"plan {plan} expert {e} token {t}")
+        else:
+            assert np.all(np.isnan(y[0])), (plan, e, t)
+
+
 def test_gemv_wide_batch(stq):
     """512 pairs over 16 experts: shared and distinct experts mixed."""
     n_experts, n, k, n_tokens = 16, 256, 1024, 64
