@@ -268,6 +268,46 @@ def test_gemv_single_pair_valid_and_invalid(stq, monkeypatch, plan):
             assert np.all(np.isnan(y[0])), (plan, e, t)
 
 
+@pytest.mark.parametrize("xdtype,plan", [("bf16", None), ("bf16", "1,3"), ("f32", None), ("f32", "2,2")])
+def test_gemv_units_numbered_by_cost_class(stq, monkeypatch, xdtype, plan):
+    """More workgroups than the CUs keep resident (300 pairs x 4 row tiles):
+    the device numbers units by cost class (experts with 5+, 3-4, 2, 1
+    tokens, then parted experts).  Experts with 1-9 tokens, invalid ids and
+    pairs in random order; every pair within 1e-3 * A of the oracle, invalid
+    pairs NaN, and a repeat call bit-equal."""
+    if plan:
+        monkeypatch.setenv("STQ_GEMV_PLAN", plan)
+    else:
+        monkeypatch.delenv("STQ_GEMV_PLAN", raising=False)
+    rng = np.random.default_rng(66)
+    n_experts, n, k, n_tokens = 60, 2048, 512, 24
+    rb = O.row_bytes(k)
+    table = np.concatenate([O.quantize_rows(S.gaussian_weights(1400 + e, n, k), None).reshape(-1)
+                            for e in range(n_experts)])
+    counts = rng.integers(1, 10, size=n_experts)
+    counts = counts * (rng.random(n_experts) < 0.8)           # some experts idle
+    pe = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    pt = np.concatenate([rng.choice(n_tokens, c, replace=False) for c in counts]).astype(np.int32)
+    pe = np.concatenate([pe, np.array([n_experts, -1, 3], np.int32)])
+    pt = np.concatenate([pt, np.array([0, 1, n_tokens], np.int32)])
+    perm = rng.permutation(pe.size)
+    pe, pt = pe[perm], pt[perm]
+    assert 200 <= pe.size <= 512
+    xb, xf = S.bf16_normal(rng, (n_tokens, k))
+    x = dev(xb.view(np.int16)).view(torch.bfloat16) if xdtype == "bf16" else dev(xf)
+    y = host(stq.gemv(dev(table), n * rb, n_experts, n, k, x, dev(pe), dev(pt)))
+    for i in range(pe.size):
+        e, t = int(pe[i]), int(pt[i])
+        if not (0 <= e < n_experts and 0 <= t < n_tokens):
+            assert np.all(np.isnan(y[i])), i
+            continue
+        raw = table[e * n * rb:(e + 1) * n * rb]
+        check_close(y[i], O.gemv(raw, n, k, xf[t]), O.tolerance_scale(raw, n, k, xf[t])[0], GEMV_TOL,
+                    f"{xdtype} plan {plan} pair {i} (expert {e}, {counts[e]} tokens)")
+    y2 = host(stq.gemv(dev(table), n * rb, n_experts, n, k, x, dev(pe), dev(pt)))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 def test_gemv_wide_batch(stq):
     """512 pairs over 16 experts: shared and distinct experts mixed."""
     n_experts, n, k, n_tokens = 16, 256, 1024, 64
