@@ -143,7 +143,10 @@ stq_status stq_dequantize_rows(const uint8_t* q, int64_t n_rows, int64_t k, floa
  * per call from the shapes and the CU count of the device `stream` runs on;
  * the environment variable STQ_GEMV_PLAN="s,p" (1 <= s <= k/256 splits,
  * 1 <= p <= 8 parts) replaces that choice, for tuning and tests.  Results
- * meet the same tolerance under every plan; their bits depend on the plan. */
+ * meet the same tolerance under every plan; their bits depend on the plan
+ * and on the pass form (with bf16 rows and at least as many pairs as
+ * experts, a pass of 3 or more tokens runs on the matrix cores), so the same
+ * bits on devices of different sizes need the same plan (STQ_GEMV_PLAN). */
 stq_status stq_gemv(const uint8_t* w_table, int64_t expert_stride_bytes, int64_t n_experts,
                     int64_t n, int64_t k, const void* x, int x_dtype, int64_t x_row_stride,
                     int64_t n_tokens, const int32_t* pair_expert, const int32_t* pair_token,
