@@ -645,7 +645,8 @@ def main() -> int:
         "roofline_gemm": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
                           "traffic": traffic_gemm, "kernel": "grouped_gemm_kernel (stq_grouped_gemm)",
-                          "flop_per_launch": gemm_flop, "avg_launch_us": round(1e3 * gemm_avg, 1)},
+                          "flop_per_launch": gemm_flop, "avg_launch_us": round(1e3 * gemm_avg, 1),
+                          "launch_us_min_max": [round(1e3 * min(gemm_ms), 1), round(1e3 * max(gemm_ms), 1)]},
         "gemv_sweep": per_batch,
     }
     ffn = {}
