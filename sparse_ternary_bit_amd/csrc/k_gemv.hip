@@ -287,7 +287,10 @@ __device__ __forceinline__ void block_dot_pairs(const char* tab, const Block& bl
   for (int m = 0; m < MC; ++m) acc[m] = fmaf(d, bs[m], acc[m]);
 }
 
-// Sum over the 64 groups of one block of table[code], for MC tokens.
+// Sum over the 64 groups of one block of table[code], for MC tokens.  A code
+// word's 8 table reads per token are all issued before its adds (left to
+// itself the scheduler may interleave each read with its add and wait on
+// every read).  Each token's sums are added in group order.
 template <int MC>
 __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, float (&acc)[kMT]) {
   static_assert(MC * kTabBytes <= kBufBytes, "one-token tables of the pass fit a buffer");
@@ -295,8 +298,8 @@ __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, flo
   float bs[MC];
 #pragma unroll
   for (int m = 0; m < MC; ++m) bs[m] = 0.0f;
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
+  // word w's reads: v[m][2j] for group 8w+j, v[m][2j+1] for group 8w+4+j
+  auto reads = [&](int w, float (&v)[MC][8]) {
     const uint32_t Q = blk.qs[w];
     const uint32_t Hs = blk.qh[w >> 2] << (6 - 2 * (w & 3));
     // byte j of cl / cu = 4 * code of group 8w+j / 8w+4+j
@@ -312,10 +315,27 @@ __device__ __forceinline__ void block_dot(const char* tab, const Block& blk, flo
       const uint32_t ou = __builtin_amdgcn_ubfe(cu, 8 * j, 8);
 #pragma unroll
       for (int m = 0; m < MC; ++m) {
-        bs[m] += *reinterpret_cast<const float*>(tab + ol + (m * kTabBytes + (8 * w + j) * kGrp1));
-        bs[m] += *reinterpret_cast<const float*>(tab + ou + (m * kTabBytes + (8 * w + 4 + j) * kGrp1));
+        v[m][2 * j] = *reinterpret_cast<const float*>(tab + ol + (m * kTabBytes + (8 * w + j) * kGrp1));
+        v[m][2 * j + 1] = *reinterpret_cast<const float*>(tab + ou + (m * kTabBytes + (8 * w + 4 + j) * kGrp1));
       }
     }
+  };
+  auto adds = [&](const float (&v)[MC][8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int m = 0; m < MC; ++m) {
+        bs[m] += v[m][2 * j];
+        bs[m] += v[m][2 * j + 1];
+      }
+  };
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float v[MC][8];
+    reads(w, v);
+    __builtin_amdgcn_sched_barrier(0);
+    adds(v);
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int m = 0; m < MC; ++m) acc[m] = fmaf(d, bs[m], acc[m]);
