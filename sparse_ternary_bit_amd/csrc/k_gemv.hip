@@ -272,6 +272,10 @@ __device__ __forceinline__ void block_dot_pairs(const char* tab, const Block& bl
         vu[j][p] = *reinterpret_cast<const float2*>(tab + ou + (p * kPairStride + (8 * w + 4 + j) * kGrp2));
       }
     }
+    // keep the word's reads ahead of its adds and the next word's reads
+    // behind them (hoisting several words' reads runs out of registers and
+    // forces waits for every read in flight)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -282,6 +286,7 @@ __device__ __forceinline__ void block_dot_pairs(const char* tab, const Block& bl
         bs[2 * p + 1] += vu[j][p].y;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int m = 0; m < MC; ++m) acc[m] = fmaf(d, bs[m], acc[m]);
