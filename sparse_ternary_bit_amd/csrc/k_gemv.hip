@@ -117,6 +117,8 @@ struct Shared {
   int lead;
   int sub;
   int nsub;
+  int lead_m;  // valid pairs of the lead's expert when the search counted them, else 0
+  int lead_t;  // the lead's token
   int flag;
   unsigned long long ball[kWaves];
   int wsum[kWaves];
@@ -644,10 +646,15 @@ __device__ __forceinline__ void run_chunk_mfma(const KArgs& a, Shared& sh, const
 // grid that deep covers them.
 constexpr int kLeadExperts = static_cast<int>(sizeof(Shared::tab) / (2 * sizeof(int)));
 
-__device__ __forceinline__ bool pair_valid(const KArgs& a, int q, int& e) {
+__device__ __forceinline__ bool pair_valid(const KArgs& a, int q, int& e, int& t) {
   e = pair_expert(a, q);
-  const int t = pair_token(a, q);
+  t = pair_token(a, q);
   return e >= 0 && e < a.n_experts && t >= 0 && t < a.n_tokens;
+}
+
+__device__ __forceinline__ bool pair_valid(const KArgs& a, int q, int& e) {
+  int t;
+  return pair_valid(a, q, e, t);
 }
 
 // With at most kLeadExperts experts: the first valid pair and the pair count
@@ -662,12 +669,16 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
   const bool parts = a.max_sub > 1;  // else every leading pair is one unit
   // pair counts order the units of one chunk and size an expert's parts
   const bool ordered = a.order && a.n_pairs <= kRows;
-  const bool counts = parts || ordered;
+  // (one chunk: also to spare a one-pair expert's unit the pair scan)
+  const bool counts = parts || a.n_pairs <= kRows;
   for (int e = tid; e < a.n_experts; e += kRows) {
     first[e] = 0x7FFFFFFF;
     if (counts) count[e] = 0;
   }
-  if (tid == 0) sh.lead = -1;
+  if (tid == 0) {
+    sh.lead = -1;
+    sh.lead_m = 0;
+  }
   __syncthreads();
   for (int q = tid; q < a.n_pairs; q += kRows) {
     int e;
@@ -687,8 +698,8 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
     // bit by bit over ballots; a wavefront's five class totals are packed 10
     // bits apiece (at most as many units as pairs, so at most 512).
     const int q = tid;
-    int e = -1;
-    const bool lead = q < a.n_pairs && pair_valid(a, q, e) && first[e] == q;
+    int e = -1, t = 0;
+    const bool lead = q < a.n_pairs && pair_valid(a, q, e, t) && first[e] == q;
     const int m = lead ? count[e] : 0;
     const int units = lead ? (parts ? min(m, a.max_sub) : 1) : 0;
     const int cls = units > 1 ? 4 : m >= 5 ? 0 : m >= 3 ? 1 : m == 2 ? 2 : 3;
@@ -719,6 +730,8 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
       sh.lead = q;
       sh.sub = z - first_unit;
       sh.nsub = units;
+      sh.lead_m = m;
+      sh.lead_t = t;
     }
     __syncthreads();  // sh.ball is read above and rewritten by the gather; sh.lead is visible
     return sh.lead;
@@ -728,8 +741,8 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
   int base = 0;
   for (int c = 0; c < a.n_pairs && base <= z; c += kRows) {
     const int q = c + tid;
-    int e = -1;
-    const bool lead = q < a.n_pairs && pair_valid(a, q, e) && first[e] == q;
+    int e = -1, t = 0;
+    const bool lead = q < a.n_pairs && pair_valid(a, q, e, t) && first[e] == q;
     const int units = lead ? (parts ? min(count[e], a.max_sub) : 1) : 0;
     // inclusive prefix sum of the unit counts over the wavefront (a ballot
     // count when every count is 0 or 1), then over the waves
@@ -758,11 +771,13 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
       sh.lead = q;
       sh.sub = z - first_unit;
       sh.nsub = units;
+      sh.lead_m = counts ? count[e] : 0;
+      sh.lead_t = t;
     }
     base += total;
     __syncthreads();  // sh.wsum is rewritten by the next chunk
   }
-  return sh.lead;  // sh.lead, sh.sub and sh.nsub are not written again in this launch
+  return sh.lead;  // sh.lead, sh.sub, sh.nsub, sh.lead_m and sh.lead_t are not written again in this launch
 }
 
 // Beyond kLeadExperts experts: workgroup z serves pair z, as its expert's
@@ -839,6 +854,9 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
   const bool parts = a.max_sub > 1 && !single;
   const int sub = parts ? __builtin_amdgcn_readfirstlane(sh.sub) : 0;
   const int nsub = parts ? __builtin_amdgcn_readfirstlane(sh.nsub) : 1;
+  // the unit's expert has one valid pair, p (a single-pair call, or one the
+  // search counted): its pass is known without the pair scan
+  const bool one = single || (a.n_experts <= kLeadExperts && __builtin_amdgcn_readfirstlane(sh.lead_m) == 1);
 
   const uint8_t* wexp = a.w + static_cast<int64_t>(e) * a.estride;
   // blocks of split `split`, then part `sub` of them (a part is empty only when the last
@@ -853,12 +871,12 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
 
   int cursor = p;
   for (;;) {
-    if (single) {
+    if (one) {
       if (tid == 0) {
-        sh.mc = cursor == 0 ? 1 : 0;
-        sh.next = 1;
-        sh.pairs[0] = 0;
-        const int t0 = pair_token(a, 0);
+        sh.mc = cursor == p ? 1 : 0;
+        sh.next = a.n_pairs;
+        sh.pairs[0] = p;
+        const int t0 = single ? pair_token(a, 0) : sh.lead_t;
         for (int m = 0; m < kMT2; ++m) sh.toks[m] = t0;
       }
       __syncthreads();
