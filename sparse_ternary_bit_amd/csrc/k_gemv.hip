@@ -118,7 +118,6 @@ struct Shared {
   int sub;
   int nsub;
   int lead_m;  // valid pairs of the lead's expert when the search counted them, else 0
-  int lead_t;  // the lead's token
   int flag;
   unsigned long long ball[kWaves];
   int wsum[kWaves];
@@ -731,7 +730,10 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
       sh.sub = z - first_unit;
       sh.nsub = units;
       sh.lead_m = m;
-      sh.lead_t = t;
+      if (m == 1) {  // the pass of a one-pair expert: this pair alone
+        sh.pairs[0] = q;
+        for (int k = 0; k < kMT2; ++k) sh.toks[k] = t;
+      }
     }
     __syncthreads();  // sh.ball is read above and rewritten by the gather; sh.lead is visible
     return sh.lead;
@@ -771,13 +773,17 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
       sh.lead = q;
       sh.sub = z - first_unit;
       sh.nsub = units;
-      sh.lead_m = counts ? count[e] : 0;
-      sh.lead_t = t;
+      const int m = counts ? count[e] : 0;
+      sh.lead_m = m;
+      if (m == 1) {  // the pass of a one-pair expert: this pair alone
+        sh.pairs[0] = q;
+        for (int k = 0; k < kMT2; ++k) sh.toks[k] = t;
+      }
     }
     base += total;
     __syncthreads();  // sh.wsum is rewritten by the next chunk
   }
-  return sh.lead;  // sh.lead, sh.sub, sh.nsub, sh.lead_m and sh.lead_t are not written again in this launch
+  return sh.lead;  // sh.lead, sh.sub, sh.nsub and sh.lead_m are not written again in this launch
 }
 
 // Beyond kLeadExperts experts: workgroup z serves pair z, as its expert's
@@ -869,23 +875,26 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
   const int n_slots = a.splits * nsub;
   const int slot = split * nsub + sub;
 
+  // one pass of the pair alone: the search placed it in sh.pairs / sh.toks
+  // (published by its last barrier); a single-pair call places it here
+  if (single) {
+    if (tid == 0) {
+      sh.pairs[0] = 0;
+      const int t0 = pair_token(a, 0);
+      for (int m = 0; m < kMT2; ++m) sh.toks[m] = t0;
+    }
+    __syncthreads();
+  }
   int cursor = p;
   for (;;) {
     if (one) {
-      if (tid == 0) {
-        sh.mc = cursor == p ? 1 : 0;
-        sh.next = a.n_pairs;
-        sh.pairs[0] = p;
-        const int t0 = single ? pair_token(a, 0) : sh.lead_t;
-        for (int m = 0; m < kMT2; ++m) sh.toks[m] = t0;
-      }
-      __syncthreads();
+      if (cursor != p) break;  // its one pass is done
     } else {
       gather<kMfma ? kMT2 : kMT>(a, sh, e, cursor);
     }
-    const int mc = __builtin_amdgcn_readfirstlane(sh.mc);
+    const int mc = one ? 1 : __builtin_amdgcn_readfirstlane(sh.mc);
     if (mc == 0) break;
-    cursor = __builtin_amdgcn_readfirstlane(sh.next);
+    cursor = one ? a.n_pairs : __builtin_amdgcn_readfirstlane(sh.next);
     auto store = [&](const auto& acc) {
       constexpr int kN = sizeof(acc) / sizeof(float);
       if (row_ok) {
@@ -919,7 +928,7 @@ __device__ __forceinline__ void gemv_main(const KArgs& a) {
     }
     // the reduction learns each pair's part count from the first unit of its expert
     if (a.pair_sub && split == 0 && sub == 0 && blockIdx.x == 0 && tid < mc) a.pair_sub[sh.pairs[tid]] = nsub;
-    __syncthreads();  // sh.pairs is rewritten by the next gather
+    if (!one) __syncthreads();  // sh.pairs is rewritten by the next gather
   }
 }
 
