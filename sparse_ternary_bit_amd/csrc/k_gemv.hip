@@ -679,9 +679,18 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
     sh.lead_m = 0;
   }
   __syncthreads();
+  // this thread's pair of the first chunk (q = tid), kept for the ranking
+  int my_e = -1, my_t = 0;
+  bool my_valid = false;
   for (int q = tid; q < a.n_pairs; q += kRows) {
-    int e;
-    if (pair_valid(a, q, e)) {
+    int e, t;
+    const bool v = pair_valid(a, q, e, t);
+    if (q == tid) {
+      my_e = e;
+      my_t = t;
+      my_valid = v;
+    }
+    if (v) {
       atomicMin(&first[e], q);
       if (counts) atomicAdd(&count[e], 1);
     }
@@ -693,12 +702,13 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
     // first, so that the last workgroups to start are short ones: whole
     // experts with 5+, 3-4, 2, 1 tokens, then the parts of parted experts
     // (each a fraction of its expert's k range).  Within a class, leading
-    // pairs in pair order.  A lane's units (at most kMaxSub = 8) are summed
-    // bit by bit over ballots; a wavefront's five class totals are packed 10
-    // bits apiece (at most as many units as pairs, so at most 512).
+    // pairs in pair order.  A whole expert is one unit (one ballot per
+    // class); a parted expert's units (at most kMaxSub = 8) are summed bit by
+    // bit over ballots; a wavefront's five class totals are packed 10 bits
+    // apiece (at most as many units as pairs, so at most 512).
     const int q = tid;
-    int e = -1, t = 0;
-    const bool lead = q < a.n_pairs && pair_valid(a, q, e, t) && first[e] == q;
+    const int e = my_e, t = my_t;
+    const bool lead = my_valid && first[e] == q;
     const int m = lead ? count[e] : 0;
     const int units = lead ? (parts ? min(m, a.max_sub) : 1) : 0;
     const int cls = units > 1 ? 4 : m >= 5 ? 0 : m >= 3 ? 1 : m == 2 ? 2 : 3;
@@ -706,13 +716,18 @@ __device__ int find_unit(const KArgs& a, Shared& sh, int z) {
     const int nbits = parts ? 4 : 1;
     int lane_before = 0;               // units of earlier lanes of this lane's class
     unsigned long long wave_tot = 0;   // the wavefront's class totals, packed
+    // classes 0-3 are whole experts (one unit each): one ballot per class
 #pragma unroll
-    for (int c = 0; c < 5; ++c) {
-      for (int b = 0; b < nbits; ++b) {
-        const unsigned long long bal = __ballot(cls == c && ((units >> b) & 1));
-        if (cls == c) lane_before += __popcll(bal & below) << b;
-        wave_tot += static_cast<unsigned long long>(__popcll(bal)) << (10 * c + b);
-      }
+    for (int c = 0; c < 4; ++c) {
+      const unsigned long long bal = __ballot(cls == c && units > 0);
+      if (cls == c) lane_before += __popcll(bal & below);
+      wave_tot += static_cast<unsigned long long>(__popcll(bal)) << (10 * c);
+    }
+    // class 4 (parted experts): the unit counts bit by bit
+    for (int b = 0; b < nbits; ++b) {
+      const unsigned long long bal = __ballot(cls == 4 && ((units >> b) & 1));
+      if (cls == 4) lane_before += __popcll(bal & below) << b;
+      wave_tot += static_cast<unsigned long long>(__popcll(bal)) << (40 + b);
     }
     if (lane == 0) sh.ball[wave] = wave_tot;
     __syncthreads();
