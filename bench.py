@@ -31,6 +31,10 @@ After the timed steps, reported beside the headline (not part of `value`):
     prefill's total shape through the vendor library (torch.matmul), the
     matrix-core rate this GPU reaches on a plain contraction;
   * `stream_read_GB/s`: the library's plain streaming read of 2 GiB;
+  * `roofline_gemm.mfma_loop_TFLOP/s`: a loop of independent bf16 MFMAs with
+    no memory traffic, the matrix-core rate this GPU sustains;
+  * `lds_probe`: LDS reads per ns per compute unit in the two forms the
+    grouped GEMM issues (16-byte activation reads, pattern-table read pairs);
   * `cpu_baseline`: the oracle, single-threaded, on bounded samples (GEMV,
     MoE decode step, encoder, grouped GEMM).
 
@@ -452,6 +456,34 @@ def main() -> int:
     stream_read_gbs = 5 * big.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
     del big, sink
 
+    # matrix-core and LDS references beside the grouped GEMM: a loop of
+    # independent bf16 MFMAs (no memory traffic), and LDS reads of the two
+    # forms the GEMM issues (16-byte activation reads, pattern-table read pairs)
+    n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    fsink = torch.zeros(1, dtype=torch.float32, device=dev)
+    isink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+    MFMA_ROUNDS, LDS_ROUNDS = 512, 1024
+    t_mfma = timed(lambda: stq.mfma_loop_probe(MFMA_ROUNDS, fsink))
+    mfma_loop_tflops = stq.MFMA_PROBE_FLOP_PER_ROUND * MFMA_ROUNDS / t_mfma / 1e12
+    lds = {"cus": n_cus}
+    for mode, name, nbytes in ((0, "b128", 1024), (1, "read2_b32", 512)):
+        t = timed(lambda: stq.lds_read_probe(mode, LDS_ROUNDS, isink))
+        per_ns = stq.LDS_PROBE_READS_PER_ROUND * LDS_ROUNDS / (t * 1e9) / n_cus
+        lds[f"{name}_reads_per_ns_per_CU"] = round(per_ns, 3)
+        lds[f"{name}_bytes_per_ns_per_CU"] = round(per_ns * nbytes, 1)
+    del fsink, isink
+
     enc_out = None
     if not args.no_encode:
         # encoder as a layer-scale workload: 8 experts' fp32 gate/up weights drawn
@@ -646,7 +678,10 @@ def main() -> int:
                           "unit": "TFLOP/s", "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
                           "traffic": traffic_gemm, "kernel": "grouped_gemm_kernel (stq_grouped_gemm)",
                           "flop_per_launch": gemm_flop, "avg_launch_us": round(1e3 * gemm_avg, 1),
-                          "launch_us_min_max": [round(1e3 * min(gemm_ms), 1), round(1e3 * max(gemm_ms), 1)]},
+                          "launch_us_min_max": [round(1e3 * min(gemm_ms), 1), round(1e3 * max(gemm_ms), 1)],
+                          "mfma_loop_TFLOP/s": round(mfma_loop_tflops, 1),
+                          "frac_of_mfma_loop": round(gemm_tflops / mfma_loop_tflops, 4)},
+        "lds_probe": lds,
         "gemv_sweep": per_batch,
     }
     ffn = {}

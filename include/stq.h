@@ -312,6 +312,30 @@ stq_status stq_greedy_allocation(const double* gain, const double* extra_bytes, 
  * meaningless). */
 stq_status stq_stream_read_probe(const void* buf, int64_t bytes, uint32_t* sink, stq_stream_t stream);
 
+/* Measurement helper, not part of the method: the matrix-core reference
+ * beside the grouped GEMM's MFMA roofline.  Launches 4096 workgroups of 4
+ * wavefronts; each wavefront runs `rounds` rounds of 8 independent
+ * v_mfma_f32_16x16x32_bf16 (16,384 flops each) with no memory traffic, so a
+ * launch does STQ_MFMA_PROBE_FLOP_PER_ROUND * rounds flops.  `rounds` >= 0
+ * (0 launches nothing); `sink` is one device float that is never written in
+ * practice (its value is meaningless). */
+#define STQ_MFMA_PROBE_FLOP_PER_ROUND 2147483648.0
+stq_status stq_mfma_loop_probe(int64_t rounds, float* sink, stq_stream_t stream);
+
+/* Measurement helper, not part of the method: the LDS read rate beside the
+ * grouped GEMM's operand reads.  Launches 4096 workgroups of 4 wavefronts;
+ * each workgroup fills a 32 KB LDS buffer once, then each wavefront runs
+ * `rounds` rounds of 8 LDS reads, each folded into a register (no other
+ * memory traffic):
+ *   mode 0: ds_read_b128, the 64 lanes reading one contiguous 1 KB run
+ *           (conflict free), the form of the GEMM's activation reads;
+ *   mode 1: ds_read2_b32 at a per-lane code 0..31 of a 32-entry table and
+ *           32 words further (the form of the GEMM's pattern reads).
+ * A launch issues STQ_LDS_PROBE_READS_PER_ROUND * rounds wavefront LDS
+ * instructions.  `mode` 0 or 1, `rounds` >= 0; `sink` as above (uint32). */
+#define STQ_LDS_PROBE_READS_PER_ROUND 131072
+stq_status stq_lds_read_probe(int mode, int64_t rounds, uint32_t* sink, stq_stream_t stream);
+
 /* Static text of a status code. */
 const char* stq_status_string(stq_status s);
 

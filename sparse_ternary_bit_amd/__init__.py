@@ -18,13 +18,17 @@ __all__ = [
     "row_bytes", "quantize_rows", "dequantize_rows", "gemv", "gemv_noalloc", "gemv_plan", "grouped_gemm",
     "moe_ffn_decode",
     "moe_ffn_workspace", "layer_errors", "layer_errors_workspace", "q2_roundtrip", "greedy_allocation",
-    "stream_read_probe",
+    "stream_read_probe", "mfma_loop_probe", "lds_read_probe", "MFMA_PROBE_FLOP_PER_ROUND",
+    "LDS_PROBE_READS_PER_ROUND",
 ]
 
 QK = 256
 BLOCK_BYTES = 42
 ENC_WLS, ENC_AMAX = 0, 1
 X_F32, X_BF16 = 0, 1
+# work of one round of the measurement probes (include/stq.h)
+MFMA_PROBE_FLOP_PER_ROUND = 2147483648.0
+LDS_PROBE_READS_PER_ROUND = 131072
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libstq.so")
@@ -93,6 +97,10 @@ def lib() -> ctypes.CDLL:
     L.stq_greedy_allocation.restype = _c_int
     L.stq_stream_read_probe.argtypes = [_c_vp, _c_i64, _c_vp, _c_vp]
     L.stq_stream_read_probe.restype = _c_int
+    L.stq_mfma_loop_probe.argtypes = [_c_i64, _c_vp, _c_vp]
+    L.stq_mfma_loop_probe.restype = _c_int
+    L.stq_lds_read_probe.argtypes = [_c_int, _c_i64, _c_vp, _c_vp]
+    L.stq_lds_read_probe.restype = _c_int
     _lib = L
     return L
 
@@ -424,3 +432,18 @@ def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
     nbytes = buf.numel() * buf.element_size()
     _check("stq_stream_read_probe", lib().stq_stream_read_probe(buf.data_ptr(), nbytes - nbytes % 16,
                                                                 sink.data_ptr(), _stream()))
+
+
+def mfma_loop_probe(rounds: int, sink: torch.Tensor) -> None:
+    """Matrix-core reference: MFMA_PROBE_FLOP_PER_ROUND * rounds flops of
+    bf16 MFMAs with no memory traffic; `sink` is a one-element float32 GPU tensor."""
+    _on_gpu("sink", sink, torch.float32)
+    _check("stq_mfma_loop_probe", lib().stq_mfma_loop_probe(int(rounds), sink.data_ptr(), _stream()))
+
+
+def lds_read_probe(mode: int, rounds: int, sink: torch.Tensor) -> None:
+    """LDS read reference: LDS_PROBE_READS_PER_ROUND * rounds wavefront LDS
+    reads, 16-byte contiguous (mode 0) or two 4-byte table reads at a code
+    (mode 1); `sink` is a one-element int32 GPU tensor."""
+    _on_gpu("sink", sink, torch.int32)
+    _check("stq_lds_read_probe", lib().stq_lds_read_probe(int(mode), int(rounds), sink.data_ptr(), _stream()))

@@ -19,8 +19,11 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libstq.so")
 
 SOURCES = ["stq_api.hip", "k_codec.hip", "k_gemv.hip", "k_gemm.hip", "k_moe.hip", "k_sens.hip", "k_probe.hip"]
-# per-file extra flags: the encoders must not contract fp64 arithmetic
-EXTRA = {"k_codec.hip": ["-ffp-contract=off"], "k_sens.hip": ["-ffp-contract=off"]}
+# per-file extra flags: the encoders must not contract fp64 arithmetic; the
+# matrix-core probe keeps its accumulators in VGPRs (in the AGPR form the
+# compiler moves them between the two files every round)
+EXTRA = {"k_codec.hip": ["-ffp-contract=off"], "k_sens.hip": ["-ffp-contract=off"],
+         "k_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 COMMON = [
     "--offload-arch=gfx950",

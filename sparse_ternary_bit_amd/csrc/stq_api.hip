@@ -390,6 +390,32 @@ stq_status stq_stream_read_probe(const void* buf, int64_t bytes, uint32_t* sink,
   return ok();
 }
 
+static_assert(STQ_MFMA_PROBE_FLOP_PER_ROUND == 4.0 * stq::kMfmaProbeGrid * stq::kMfmaChains * 16384.0,
+              "the MFMA probe's stated work per round");
+static_assert(STQ_LDS_PROBE_READS_PER_ROUND == 4 * stq::kLdsProbeGrid * stq::kLdsReads,
+              "the LDS probe's stated reads per round");
+
+stq_status stq_mfma_loop_probe(int64_t rounds, float* sink, stq_stream_t stream) {
+  if (rounds < 0) return fail(STQ_E_ARG, "stq_mfma_loop_probe: rounds must be >= 0");
+  if (rounds == 0) return ok();
+  if (!sink) return fail(STQ_E_ARG, "stq_mfma_loop_probe: null sink");
+  if (!aligned(sink, 4)) return fail(STQ_E_ALIGN, "stq_mfma_loop_probe: sink must be 4-byte aligned");
+  hipError_t e = stq::launch_mfma_loop(rounds, sink, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stq_mfma_loop_probe launch");
+  return ok();
+}
+
+stq_status stq_lds_read_probe(int mode, int64_t rounds, uint32_t* sink, stq_stream_t stream) {
+  if (mode != 0 && mode != 1) return fail(STQ_E_ARG, "stq_lds_read_probe: mode must be 0 or 1");
+  if (rounds < 0) return fail(STQ_E_ARG, "stq_lds_read_probe: rounds must be >= 0");
+  if (rounds == 0) return ok();
+  if (!sink) return fail(STQ_E_ARG, "stq_lds_read_probe: null sink");
+  if (!aligned(sink, 4)) return fail(STQ_E_ALIGN, "stq_lds_read_probe: sink must be 4-byte aligned");
+  hipError_t e = stq::launch_lds_read(mode, rounds, sink, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stq_lds_read_probe launch");
+  return ok();
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

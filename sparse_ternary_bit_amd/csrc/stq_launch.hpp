@@ -102,4 +102,14 @@ hipError_t launch_q2_roundtrip(const float* w, int64_t n_rows, int64_t k, float*
 // Streaming-read reference (measurement only): reads `bytes` bytes of `buf`
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 
+// Matrix-core and LDS references (measurement only).  Their shapes are the
+// ones stq.h states, so that callers can count the work of a launch.
+constexpr int kMfmaProbeGrid = 4096;  // workgroups of 4 wavefronts
+constexpr int kMfmaChains = 8;        // independent MFMAs per wavefront and round
+constexpr int kLdsProbeGrid = 4096;   // workgroups of 4 wavefronts
+constexpr int kLdsReads = 8;          // LDS reads per wavefront and round
+constexpr int kLdsProbeWords = 2048;  // 16-byte words of LDS per workgroup (32 KB)
+hipError_t launch_mfma_loop(int64_t iters, float* sink, hipStream_t s);
+hipError_t launch_lds_read(int mode, int64_t iters, uint32_t* sink, hipStream_t s);
+
 }  // namespace stq

@@ -392,6 +392,28 @@ def test_stream_read_probe_rejects_bad_arguments(L):
     assert L.stq_stream_read_probe(None, 0, None, None) == 0
 
 
+def test_mfma_and_lds_probes_reject_bad_arguments(L):
+    import sparse_ternary_bit_amd as stq
+    mfma = L.stq_mfma_loop_probe
+    assert mfma(-1, FAKE, None) == 1
+    assert mfma(4, None, None) == 1
+    assert mfma(4, FAKE + 2, None) == 3
+    assert mfma(0, None, None) == 0  # nothing to launch
+    lds = L.stq_lds_read_probe
+    assert lds(2, 4, FAKE, None) == 1
+    assert lds(-1, 4, FAKE, None) == 1
+    assert lds(0, -1, FAKE, None) == 1
+    assert lds(1, 4, None, None) == 1
+    assert lds(0, 4, FAKE + 1, None) == 3
+    assert lds(1, 0, None, None) == 0
+    # the binding's work counts are the header's
+    hdr = open(os.path.join(os.path.dirname(stq.lib_path()), "..", "include", "stq.h")).read()
+    assert f"#define STQ_MFMA_PROBE_FLOP_PER_ROUND {stq.MFMA_PROBE_FLOP_PER_ROUND!r}" in hdr
+    assert f"#define STQ_LDS_PROBE_READS_PER_ROUND {stq.LDS_PROBE_READS_PER_ROUND}" in hdr
+    assert stq.MFMA_PROBE_FLOP_PER_ROUND == 4096 * 4 * 8 * (2 * 16 * 16 * 32)
+    assert stq.LDS_PROBE_READS_PER_ROUND == 4096 * 4 * 8
+
+
 def test_gemv_noalloc_checks_and_refuses_shapes_beyond_its_scratch(L, monkeypatch):
     """stq_gemv_noalloc checks its arguments like stq_gemv and refuses, before
     touching the GPU, shapes whose plan needs more than its fixed scratch."""

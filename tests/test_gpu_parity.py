@@ -686,3 +686,20 @@ def test_stream_read_probe_runs(stq):
     stq.stream_read_probe(buf[: 1000], sink)
     torch.cuda.synchronize()
     assert torch.equal(buf, before)
+
+
+def test_mfma_and_lds_probes_run(stq):
+    """The matrix-core and LDS reference kernels (measurement only) complete
+    on a few rounds and touch no memory but their sink: the MFMA sums are
+    positive, so its float sink keeps its value; the LDS sink keeps its
+    value or takes the fixed tag a fold may match."""
+    fs = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    is_ = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    stq.mfma_loop_probe(3, fs)
+    stq.mfma_loop_probe(0, fs)
+    for mode in (0, 1):
+        stq.lds_read_probe(mode, 5, is_)
+        stq.lds_read_probe(mode, 0, is_)
+    torch.cuda.synchronize()
+    assert fs.item() == 7.0
+    assert is_.item() in (7, 0x5EED5EED)
