@@ -55,6 +55,7 @@ hash matches the current sources.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -419,6 +420,12 @@ def main() -> int:
             b.record(stream)
             rec["ffn"].append((B, nbytes, a, b))
 
+    # Python's cyclic garbage collector is off while the GPU is timed (as timeit
+    # does): a full collection in this process takes up to tens of ms, and one
+    # that lands while the launch queue runs dry leaves the GPU idle between the
+    # two events of a call, which then counts as that call's time
+    gc.collect()
+    gc.disable()
     for s in range(args.warmup):
         run_step(s, {"gemv": [], "gemm": [], "ffn": []})
     torch.cuda.synchronize()
@@ -704,6 +711,7 @@ def main() -> int:
     if dense_out:
         out["roofline_gemm"].update(dense_out)
         out["roofline_gemm"]["frac_of_dense_bf16_gemm"] = round(gemm_tflops / dense_out["dense_bf16_gemm_TFLOP/s"], 4)
+    gc.enable()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
